@@ -1,0 +1,187 @@
+// C ABI entry points: argument validation, workspace layout, dispatch.
+// Every check below happens before anything is enqueued on the stream.
+#include <cstdint>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace bqmoe {
+
+static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static bool layer_ok(const moe_layer* L) {
+  if (!L) return false;
+  if (L->d <= 0 || L->inter <= 0 || L->d % 128 || L->inter % 128 || L->d > MOE_MAX_DIM ||
+      L->inter > MOE_MAX_DIM)
+    return false;
+  if (L->n_experts < 1 || L->n_experts > MOE_MAX_EXPERTS) return false;
+  if (L->top_k < 1 || L->top_k > MOE_MAX_TOPK || L->top_k > L->n_experts) return false;
+  if (L->n_shared < 0 || L->n_shared > 1) return false;
+  if (!qtype_levels(L->q_gate) || !qtype_levels(L->q_up) || !qtype_levels(L->q_down)) return false;
+  return true;
+}
+
+DecodeWs decode_ws_layout(const moe_layer* L, int T) {
+  DecodeWs w{};
+  const int k = L->top_k, d = L->d, I = L->inter, S = L->n_shared;
+  w.max_slots = (T * k < L->n_experts ? T * k : L->n_experts) + S;
+  w.rows = T * k + T * S;
+  size_t o = 0;
+  w.slots = o;
+  o = al256(o + sizeof(int32_t) * (1 + 3 * (size_t)w.max_slots));
+  w.counters = o;
+  o = al256(o + sizeof(uint32_t) * (size_t)(d / 64));
+  w.xs = o;
+  o = al256(o + 2 * (size_t)T * d);
+  w.xsum = o;
+  o = al256(o + 8 * (size_t)T * (d / 32));
+  w.hs = o;
+  o = al256(o + 2 * (size_t)w.rows * I);
+  w.hsum = o;
+  o = al256(o + 8 * (size_t)w.rows * (I / 32));
+  w.y = o;
+  o = al256(o + 2 * (size_t)w.rows * d);
+  w.total = o;
+  return w;
+}
+
+PrefillWs prefill_ws_layout(const moe_layer* L, int T) {
+  PrefillWs p{};
+  const int k = L->top_k, d = L->d, I = L->inter, S = L->n_shared, E = L->n_experts;
+  p.nblk = (T + kHistTokensPerBlock - 1) / kHistTokensPerBlock;
+  const size_t rows_routed = (size_t)T * k;
+  p.rows = (int)(rows_routed + (size_t)T * S);
+  p.max_tiles = (int)(rows_routed / kPrefillTileM + (size_t)E +
+                      (S ? ((size_t)T + kPrefillTileM - 1) / kPrefillTileM : 0));
+  size_t o = 0;
+  p.ctrl = o;
+  o = al256(o + 64);
+  p.hist = o;
+  o = al256(o + sizeof(int32_t) * (size_t)p.nblk * E);
+  p.lrank = o;
+  o = al256(o + sizeof(int32_t) * rows_routed);
+  p.tiles = o;
+  o = al256(o + sizeof(int32_t) * 4 * (size_t)p.max_tiles);
+  p.xs = o;
+  o = al256(o + 2 * (size_t)T * d);
+  p.xsum = o;
+  o = al256(o + 8 * (size_t)T * (d / 32));
+  p.h = o;
+  o = al256(o + 2 * (size_t)p.rows * I);
+  p.hsum = o;
+  o = al256(o + 8 * (size_t)p.rows * (I / 32));
+  p.y = o;
+  o = al256(o + 2 * (size_t)p.rows * d);
+  p.total = o;
+  return p;
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// shared checks for the calls that take routing buffers
+static moe_status check_common(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                               const moe_routing* R, const void* ws, size_t ws_bytes,
+                               bool need_experts) {
+  if (!layer_ok(L)) {
+    if (!L) return MOE_ERR_INVALID_ARG;
+    // distinguish plain invalid values from unsupported-but-meaningful shapes
+    if (L->d <= 0 || L->inter <= 0 || L->n_experts <= 0 || L->top_k <= 0 ||
+        L->top_k > L->n_experts || L->n_shared < 0 || L->n_shared > 1)
+      return MOE_ERR_INVALID_ARG;
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)(MOE_LOGITS_GIVEN | MOE_ADD_RESIDUAL)) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * L->top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  if (!R || !R->logits || !R->topk_ids || !R->topk_w || !R->counts || !R->offsets ||
+      !R->perm_tok || !R->inv_row)
+    return MOE_ERR_INVALID_ARG;
+  if (!(flags & MOE_LOGITS_GIVEN)) {
+    if (!L->router_w || !x) return MOE_ERR_INVALID_ARG;
+  }
+  if (need_experts) {
+    const size_t eb = moe_expert_bytes(L->q_gate, L->q_up, L->q_down, L->d, L->inter);
+    if (!x || !L->experts || L->expert_stride < eb || L->expert_stride % 256 ||
+        !aligned(L->experts, 256))
+      return MOE_ERR_INVALID_ARG;
+    if (L->n_shared && (!L->shared || !aligned(L->shared, 256))) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16)) return MOE_ERR_INVALID_ARG;
+  }
+  if (!ws || ws_bytes < moe_workspace_bytes(L, T)) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace bqmoe
+
+using namespace bqmoe;
+
+extern "C" size_t moe_workspace_bytes(const moe_layer* L, int32_t T) {
+  if (!layer_ok(L) || T < 0) return 0;
+  if (T == 0) return 256;
+  size_t b = prefill_ws_layout(L, T).total;
+  if (T <= MOE_MAX_DECODE_TOKENS) {
+    const size_t dcd = decode_ws_layout(L, T).total;
+    if (dcd > b) b = dcd;
+  }
+  return b;
+}
+
+extern "C" moe_status moe_route_topk(const moe_layer* L, const uint16_t* x, int32_t T,
+                                     uint32_t flags, moe_routing* R, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (T == 0 && L && R) return MOE_OK;
+  moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, false);
+  if (st != MOE_OK) return st;
+  const PrefillWs P = prefill_ws_layout(L, T);
+  return launch_route_generic(L, x, T, flags, R, (uint8_t*)ws, P, stream) ? MOE_ERR_DEVICE
+                                                                         : MOE_OK;
+}
+
+extern "C" moe_status moe_forward_decode(const moe_layer* L, const uint16_t* x, int32_t T,
+                                         uint32_t flags, moe_routing* R, void* ws,
+                                         size_t ws_bytes, uint16_t* out, void* stream) {
+  if (T < 1 || T > MOE_MAX_DECODE_TOKENS) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, true);
+  if (st != MOE_OK) return st;
+  if (T * L->top_k > kDecodeMaxRoutedRows || T * (L->top_k + L->n_shared) > kDecodeMaxRows)
+    return MOE_ERR_UNSUPPORTED;
+  if (!out || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)T * L->d * 2;
+  if (overlaps(x, bytes, out, bytes)) return MOE_ERR_INVALID_ARG;
+  const DecodeWs W = decode_ws_layout(L, T);
+  return launch_decode(L, x, T, flags, R, (uint8_t*)ws, W, out, stream) ? MOE_ERR_DEVICE : MOE_OK;
+}
+
+extern "C" moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T,
+                                          uint32_t flags, moe_routing* R, void* ws,
+                                          size_t ws_bytes, uint16_t* out, void* stream) {
+  if (T == 0 && L && R) return MOE_OK;
+  moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, true);
+  if (st != MOE_OK) return st;
+  if (!out || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)T * L->d * 2;
+  if (overlaps(x, bytes, out, bytes)) return MOE_ERR_INVALID_ARG;
+  const PrefillWs P = prefill_ws_layout(L, T);
+  return launch_prefill(L, x, T, flags, R, (uint8_t*)ws, P, out, stream) ? MOE_ERR_DEVICE
+                                                                        : MOE_OK;
+}
+
+extern "C" const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_BAD_CODES: return "level index outside its alphabet";
+    case MOE_ERR_DEVICE: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" int moe_abi_version(void) { return 1; }

@@ -1,0 +1,85 @@
+// Internal declarations shared by the host dispatch and the HIP kernels.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/moe.h"
+
+namespace bqmoe {
+
+inline int qtype_levels(int q) {
+  return q == MOE_Q_TERNARY ? 3 : q == MOE_Q_INT2 ? 4 : q == MOE_Q_INT3 ? 8 : 0;
+}
+inline float qtype_offset(int q) {
+  return q == MOE_Q_TERNARY ? 1.0f : q == MOE_Q_INT2 ? 1.5f : 3.5f;
+}
+
+// Byte offsets of the regions of one packed projection.
+struct PackedLayout {
+  size_t plane0, plane1, scales, total;
+};
+bool format_shape_ok(int qtype, int64_t K, int64_t N);
+PackedLayout packed_layout(int qtype, int64_t K, int64_t N);
+
+// One projection as the kernels see it: byte offset inside an expert blob plus
+// the region offsets relative to the start of the projection.
+struct ProjDesc {
+  uint64_t off;      // from the start of the expert blob
+  uint64_t plane1;   // relative to off (3-bit only)
+  uint64_t scales;   // relative to off
+  int32_t qtype;
+  int32_t K, N;
+};
+
+// Magic-number operand encoding used by the kernels: a level u becomes the
+// bf16 value 128 + 16u (exact), activations are pre-scaled by 1/16 (exact),
+// so each product is x*(8 + u); the per-group term (8 + offset) * sum(x) is
+// removed through a second matrix-core op.  corr_const(q) = 8 + offset.
+inline float corr_const(int q) { return 8.0f + qtype_offset(q); }
+
+constexpr int kDecodeMaxRoutedRows = 64;  // T*k for the decode path
+constexpr int kDecodeMaxRows = 72;        // T*(k + n_shared) for the decode path
+
+// Workspace layouts (byte offsets from the workspace base).
+struct DecodeWs {
+  size_t slots;     // int32 [1 + 3*max_slots]: n_slots, then (expert|-1, row0, rows)
+  size_t counters;  // uint32 [d/64] combine arrival counters
+  size_t xs;        // bf16 [T][d]        x / 16
+  size_t xsum;      // bf16 [T][d/32][4]  -(hi, mid, lo) of each 32-group sum of x, 0
+  size_t hs;        // bf16 [rows][I]     h / 16
+  size_t hsum;      // bf16 [rows][I/32][4]
+  size_t y;         // bf16 [rows][d]
+  size_t total;
+  int max_slots, rows;
+};
+
+struct PrefillWs {
+  size_t hist;      // int32 [nblk][E]   per-block expert counts
+  size_t lrank;     // int32 [T*k]       rank of each row among its block's rows of that expert
+  size_t tiles;     // int32 [max_tiles][4] (expert|-1, row0, rows, 0) + int32 count (at ctrl)
+  size_t ctrl;      // int32 [16] counters
+  size_t xs;        // bf16 [T][d]        x / 16
+  size_t xsum;      // bf16 [T][d/32][4]  negated bf16 triple of each 32-group sum of x
+  size_t h;         // bf16 [rows][I]     h / 16
+  size_t hsum;      // bf16 [rows][I/32][4]
+  size_t y;         // bf16 [rows][d]
+  size_t total;
+  int nblk, max_tiles, rows;
+};
+
+constexpr int kHistTokensPerBlock = 256;  // tokens per histogram block
+constexpr int kPrefillTileM = 128;        // rows per grouped-GEMM tile
+
+DecodeWs decode_ws_layout(const moe_layer* L, int T);
+PrefillWs prefill_ws_layout(const moe_layer* L, int T);
+
+// ---------------------------------------------------------------- launchers
+// All return hipSuccess (0) or the launch error code.
+int launch_route_generic(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
+                         moe_routing* R, uint8_t* ws, const PrefillWs& P, void* stream);
+int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
+                  uint8_t* ws, const DecodeWs& W, uint16_t* out, void* stream);
+int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
+                   uint8_t* ws, const PrefillWs& P, uint16_t* out, void* stream);
+
+}  // namespace bqmoe

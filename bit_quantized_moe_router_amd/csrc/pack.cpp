@@ -1,0 +1,94 @@
+// Host-side packing of one projection into packed format v1 (see moe.h).
+//
+// The format is laid out for the decode kernels: a 512-B tile holds a 16 (n)
+// x 128 (k) block of 2-bit fields, and lane chunk L = 16q + r of a tile is
+// what wavefront lane L feeds to the matrix core for output column r and the
+// k-slots 8q..8q+7 of each 32-wide group.  Inside a lane's 32-bit word the two
+// 16-bit halves carry adjacent k-slots (s even / odd) of the same group, so a
+// single mask-and-or turns a pair of fields into a pair of bf16 operands.
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace bqmoe {
+
+static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool format_shape_ok(int qtype, int64_t K, int64_t N) {
+  return qtype_levels(qtype) > 0 && K > 0 && N > 0 && K % 128 == 0 && N % 16 == 0 &&
+         K <= (int64_t(1) << 24) && N <= (int64_t(1) << 24);
+}
+
+PackedLayout packed_layout(int qtype, int64_t K, int64_t N) {
+  PackedLayout p{};
+  if (!format_shape_ok(qtype, K, N)) return p;
+  size_t tiles = size_t(N / 16) * size_t(K / 128);
+  p.plane0 = 0;
+  size_t end = round256(tiles * 512);
+  p.plane1 = end;
+  if (qtype == MOE_Q_INT3) end = round256(end + tiles * 256);
+  p.scales = end;
+  p.total = round256(end + tiles * 128);
+  return p;
+}
+
+}  // namespace bqmoe
+
+using namespace bqmoe;
+
+extern "C" size_t moe_packed_bytes(int qtype, int64_t K, int64_t N) {
+  return packed_layout(qtype, K, N).total;
+}
+
+extern "C" size_t moe_expert_bytes(int qg, int qu, int qd, int64_t d, int64_t inter) {
+  size_t g = moe_packed_bytes(qg, d, inter), u = moe_packed_bytes(qu, d, inter),
+         dn = moe_packed_bytes(qd, inter, d);
+  if (!g || !u || !dn) return 0;
+  return g + u + dn;  // each is a multiple of 256
+}
+
+extern "C" moe_status moe_pack_weights(int qtype, int64_t K, int64_t N, const uint8_t* codes,
+                                       const uint16_t* scales, void* out, size_t out_bytes) {
+  if (!format_shape_ok(qtype, K, N)) return MOE_ERR_UNSUPPORTED;
+  if (!codes || !scales || !out) return MOE_ERR_INVALID_ARG;
+  PackedLayout lay = packed_layout(qtype, K, N);
+  if (out_bytes < lay.total) return MOE_ERR_INVALID_ARG;
+  const int levels = qtype_levels(qtype);
+  for (int64_t i = 0; i < K * N; ++i)
+    if (codes[i] >= levels) return MOE_ERR_BAD_CODES;
+
+  uint8_t* base = static_cast<uint8_t*>(out);
+  std::memset(base, 0, lay.total);
+  const int64_t NT = N / 16, KB = K / 128;
+  for (int64_t nt = 0; nt < NT; ++nt) {
+    for (int64_t kb = 0; kb < KB; ++kb) {
+      const size_t tile = size_t(nt * KB + kb);
+      uint32_t* p0 = reinterpret_cast<uint32_t*>(base + lay.plane0 + tile * 512);
+      uint32_t* p1 = reinterpret_cast<uint32_t*>(base + lay.plane1 + tile * 256);
+      uint16_t* ps = reinterpret_cast<uint16_t*>(base + lay.scales + tile * 128);
+      for (int lane = 0; lane < 64; ++lane) {
+        const int q = lane >> 4, r = lane & 15;
+        const int64_t n = nt * 16 + r;
+        const uint8_t* row = codes + n * K + kb * 128;
+        uint32_t w0[2] = {0, 0}, hi = 0;
+        for (int gb = 0; gb < 4; ++gb) {      // group inside the k-block
+          for (int s = 0; s < 8; ++s) {       // k-slot inside the lane's 8
+            const int kk = gb * 32 + q * 8 + s;
+            const uint32_t u = row[kk];
+            const int half = s & 1, pair = s >> 1;
+            const int field = 4 * (gb & 1) + pair;
+            w0[gb >> 1] |= (u & 3u) << (16 * half + 2 * field);
+            hi |= (u >> 2) << (16 * half + 4 * gb + pair);
+          }
+        }
+        p0[lane * 2 + 0] = w0[0];
+        p0[lane * 2 + 1] = w0[1];
+        if (qtype == MOE_Q_INT3) p1[lane] = hi;
+      }
+      for (int r = 0; r < 16; ++r)
+        for (int gb = 0; gb < 4; ++gb)
+          ps[r * 4 + gb] = scales[(nt * 16 + r) * (K / 32) + kb * 4 + gb];
+    }
+  }
+  return MOE_OK;
+}

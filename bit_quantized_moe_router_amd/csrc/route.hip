@@ -1,0 +1,460 @@
+// Routing kernels: router logits, top-k with softmax weights, and the stable
+// expert permutation (histogram / prefix sum / scatter with wavefront ballots).
+//
+// The pages ("Xolotl" card, README "How it works, in one paragraph") say only
+// that each token's router asks for a few experts.  The rule implemented here
+// (Reading): the k largest fp32 logits, descending, lower expert index first on
+// equal values (IEEE ==), weights = softmax over the selected k; rows are
+// grouped by expert with tokens ascending inside each expert.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace bqmoe {
+
+// ------------------------------------------------------------------ logits
+// Wave per expert, up to 8 tokens per block row (grid.y tiles the tokens).
+// Router weights are stored [E][d] so a wave streams one contiguous row.
+// With `xs` set (decode), blocks also stage x for the expert kernels:
+// xs = x/16 (exact) and, per 32-group, the sum of x split into three bf16
+// parts (negated) for the matrix-core correction term.
+__global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x, int T, int d,
+                                                       int E, const float* __restrict__ Wr,
+                                                       const float* __restrict__ bias,
+                                                       float* __restrict__ logits, int do_logits,
+                                                       uint16_t* __restrict__ xs,
+                                                       uint16_t* __restrict__ xsum) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.y * 8;
+  const int nt = min(8, T - t0);
+  if (do_logits) {
+    const int e = blockIdx.x * 4 + wave;
+    if (e < E) {
+      float acc[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+      const float* w = Wr + (size_t)e * d;
+      for (int i = lane * 4; i < d; i += 256) {
+        const float4 wv = *reinterpret_cast<const float4*>(w + i);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if (t < nt) {
+            const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + t) * d + i);
+            acc[t] = fmaf(bf16_to_f32(xv.x & 0xFFFFu), wv.x, acc[t]);
+            acc[t] = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc[t]);
+            acc[t] = fmaf(bf16_to_f32(xv.y & 0xFFFFu), wv.z, acc[t]);
+            acc[t] = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc[t]);
+          }
+        }
+      }
+      const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t < nt) {
+          const float s = wave_sum(acc[t]);
+          if (lane == 0) logits[(size_t)(t0 + t) * E + e] = s + b;
+        }
+      }
+    }
+  }
+  if (xs) {
+    // staging: one 32-lane half-wave per (token, group); pairs spread over the grid
+    const int G = d / 32;
+    const int pairs = T * G;
+    const int half = threadIdx.x >> 5, j = threadIdx.x & 31;
+    for (int p = blockIdx.x * 8 + half; p < pairs; p += gridDim.x * 8) {
+      const int t = p / G, g = p % G;
+      const uint32_t xb = x[(size_t)t * d + g * 32 + j];
+      const float xf = bf16_to_f32(xb);
+      xs[(size_t)t * d + g * 32 + j] = (uint16_t)f32_to_bf16(xf * 0.0625f);
+      float s = xf;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
+      if (j == 0) {
+        const uint32_t hi = f32_to_bf16(s);
+        const float r1 = s - bf16_to_f32(hi);
+        const uint32_t mid = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(mid);
+        const uint32_t lo = f32_to_bf16(r2);
+        uint2 v;
+        v.x = ((hi ^ 0x8000u) & 0xFFFFu) | (((mid ^ 0x8000u) & 0xFFFFu) << 16);
+        v.y = (lo ^ 0x8000u) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(xsum + ((size_t)t * G + g) * 4) = v;
+      }
+    }
+  }
+}
+
+// candidate (va, ia) ranks before (vb, ib)
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Top-k of one token's E logits by one wave.  Lane l holds experts l + 64i.
+// Returns (in lanes 0..k-1) the selected ids and weights.
+__device__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, int& my_id,
+                          float& my_w) {
+  constexpr int MAXPER = MOE_MAX_EXPERTS / 64;
+  float v[MAXPER];
+  const int per = (E + 63) / 64;
+#pragma unroll
+  for (int i = 0; i < MAXPER; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (i < per && e < E) ? L[e] : -INFINITY;
+  }
+  uint32_t taken = 0;  // bit i: v[i] already selected (or absent)
+#pragma unroll
+  for (int i = 0; i < MAXPER; ++i)
+    if (!(i < per && lane + 64 * i < E)) taken |= 1u << i;
+  float top = 0.f;
+  my_id = -1;
+  float my_v = 0.f;
+  for (int j = 0; j < k; ++j) {
+    // lane-local best
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      const int e = lane + 64 * i;
+      if (!((taken >> i) & 1u) && ranks_before(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+    // wave argmax under the same rule
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ranks_before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (j == 0) top = bv;
+    if (lane == j) {
+      my_id = bi;
+      my_v = bv;
+    }
+  }
+  // softmax over the selected k (lanes < k)
+  float ex = (lane < k) ? expf(my_v - top) : 0.f;
+  float den = wave_sum(ex);
+  my_w = ex / den;
+}
+
+// Generic top-k: wave per token.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  int id;
+  float wt;
+  wave_topk(logits + (size_t)t * E, E, k, lane, id, wt);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
+  }
+}
+
+// Lanes whose `key` (< 2^bits) equals this lane's, among `active` lanes.
+__device__ __forceinline__ uint64_t match_peers(int key, int bits, uint64_t active) {
+  uint64_t peers = active;
+  for (int b = 0; b < bits; ++b) {
+    const uint64_t m = __ballot((key >> b) & 1);
+    peers &= ((key >> b) & 1) ? m : ~m;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ int expert_bits(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b ? b : 1;
+}
+
+// Block-wide exclusive scan of n <= 2*blockDim.x ints in LDS (in place).
+// Returns the total.  blockDim.x must be a multiple of 64, at most 1024.
+__device__ int block_exclusive_scan(int* a, int n, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  const int v0 = i0 < n ? a[i0] : 0, v1 = i1 < n ? a[i1] : 0;
+  int s = v0 + v1;
+  // inclusive scan inside the wave
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int t = wave_tot[w];
+      wave_tot[w] = run;
+      run += t;
+    }
+    wave_tot[nw] = run;
+  }
+  __syncthreads();
+  const int excl = incl - s + wave_tot[wave];
+  if (i0 < n) a[i0] = excl;
+  if (i1 < n) a[i1] = excl + v0;
+  const int total = wave_tot[nw];
+  __syncthreads();
+  return total;
+}
+
+// ------------------------------------------------- decode: select + permute
+// One block of 512 threads for T <= 8 tokens: top-k per token (wave t), the
+// stable permutation of the T*k <= 64 rows (one wave, ballot matching), the
+// prefix sum over experts, and the list of active experts ("slots") in
+// ascending expert id followed by the shared expert.  Also clears the
+// combine counters of the down-projection kernel.
+__global__ __launch_bounds__(512) void k_dec_select(const float* __restrict__ logits, int T, int E,
+                                                    int k, int n_shared, int32_t* __restrict__ ids,
+                                                    float* __restrict__ wts,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm_tok,
+                                                    int32_t* __restrict__ inv_row,
+                                                    int32_t* __restrict__ slots,
+                                                    uint32_t* __restrict__ counters, int n_counters) {
+  __shared__ int s_ids[64];
+  __shared__ int s_rank[64];
+  __shared__ int s_cnt[MOE_MAX_EXPERTS];
+  __shared__ int s_off[MOE_MAX_EXPERTS];
+  __shared__ int s_flag[MOE_MAX_EXPERTS];
+  __shared__ int s_tot[17];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < n_counters; i += blockDim.x) counters[i] = 0u;
+  for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
+  if (wave < T) {
+    int id;
+    float wt;
+    wave_topk(logits + (size_t)wave * E, E, k, lane, id, wt);
+    if (lane < k) {
+      ids[(size_t)wave * k + lane] = id;
+      wts[(size_t)wave * k + lane] = wt;
+      s_ids[wave * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  const int rows = T * k;
+  if (wave == 0) {
+    const bool act = lane < rows;
+    const int e = act ? s_ids[lane] : 0;
+    const uint64_t active = __ballot(act);
+    const uint64_t peers = match_peers(e, expert_bits(E), active);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (act) {
+      s_rank[lane] = __popcll(peers & lt);
+      if ((peers & lt) == 0) s_cnt[e] = __popcll(peers);  // group leader
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    s_off[e] = s_cnt[e];
+    s_flag[e] = s_cnt[e] > 0;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_off, E, s_tot);
+  const int n_active = block_exclusive_scan(s_flag, E, s_tot);
+  for (int e = tid; e < E; e += blockDim.x) {
+    counts[e] = s_cnt[e];
+    offsets[e] = s_off[e];
+    if (s_cnt[e] > 0) {
+      const int s = s_flag[e];
+      slots[1 + 3 * s] = e;
+      slots[2 + 3 * s] = s_off[e];
+      slots[3 + 3 * s] = s_cnt[e];
+    }
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    int ns = n_active;
+    if (n_shared) {
+      slots[1 + 3 * ns] = -1;
+      slots[2 + 3 * ns] = rows;
+      slots[3 + 3 * ns] = T;
+      ++ns;
+    }
+    slots[0] = ns;
+  }
+  if (tid < rows) {
+    const int e = s_ids[tid];
+    const int pos = s_off[e] + s_rank[tid];
+    perm_tok[pos] = tid / k;
+    inv_row[tid] = pos;
+  }
+}
+
+// ------------------------------------------------ generic permutation (any T)
+// Block b handles tokens [b*256, b*256+256), i.e. rows [b*256*k, ...).  Each
+// wave takes a contiguous quarter of the block's rows in 64-row chunks; lanes
+// with equal experts are matched with ballots, so every row gets its rank
+// among the block's earlier rows of the same expert without atomics.
+__global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ ids, int T, int E, int k,
+                                              int32_t* __restrict__ hist,
+                                              int32_t* __restrict__ lrank) {
+  __shared__ int cnt[4][MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 4 * E; i += 256) cnt[i / E][i % E] = 0;
+  __syncthreads();
+  const int r_begin = blockIdx.x * kHistTokensPerBlock * k;
+  const int r_end = min(T * k, r_begin + kHistTokensPerBlock * k);
+  const int nrows = r_end - r_begin;
+  const int nchunk = (nrows + 63) / 64;
+  const int per = (nchunk + 3) / 4;
+  const int c0 = wave * per, c1 = min(nchunk, c0 + per);
+  const int bits = expert_bits(E);
+  for (int c = c0; c < c1; ++c) {
+    const int r = r_begin + c * 64 + lane;
+    const bool act = r < r_end;
+    const int e = act ? ids[r] : 0;
+    const uint64_t active = __ballot(act);
+    const uint64_t peers = match_peers(e, bits, active);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // One LDS read instruction for all lanes, then the group leaders' write: a
+    // wave's LDS accesses complete in program order, so no barrier is needed.
+    int base = 0;
+    if (act) base = cnt[wave][e];
+    if (act) lrank[r] = base + __popcll(peers & lt);
+    if (act && (peers & lt) == 0) cnt[wave][e] = base + __popcll(peers);
+  }
+  __syncthreads();
+  // per-wave bases (prefix over waves) and the block histogram
+  for (int e = tid; e < E; e += 256) {
+    int run = 0;
+    for (int w = 0; w < 4; ++w) {
+      const int c = cnt[w][e];
+      cnt[w][e] = run;
+      run += c;
+    }
+    hist[(size_t)blockIdx.x * E + e] = run;
+  }
+  __syncthreads();
+  for (int c = c0; c < c1; ++c) {
+    const int r = r_begin + c * 64 + lane;
+    if (r < r_end) lrank[r] += cnt[wave][ids[r]];
+  }
+}
+
+// Single block: per-expert exclusive scan over blocks (in place), counts,
+// offsets, and the grouped-GEMM tile list (routed experts in id order, then
+// the shared expert).
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nblk, int E, int T,
+                                               int k, int n_shared, int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ tiles,
+                                               int32_t* __restrict__ ctrl) {
+  __shared__ int s_cnt[MOE_MAX_EXPERTS];
+  __shared__ int s_off[MOE_MAX_EXPERTS];
+  __shared__ int s_nt[MOE_MAX_EXPERTS];
+  __shared__ int s_tot[17];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const size_t i = (size_t)b * E + e;
+      const int c = hist[i];
+      hist[i] = run;
+      run += c;
+    }
+    s_cnt[e] = run;
+    s_off[e] = run;
+    s_nt[e] = (run + kPrefillTileM - 1) / kPrefillTileM;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_off, E, s_tot);
+  const int ntiles = block_exclusive_scan(s_nt, E, s_tot);
+  for (int e = tid; e < E; e += blockDim.x) {
+    counts[e] = s_cnt[e];
+    offsets[e] = s_off[e];
+    const int n = (s_cnt[e] + kPrefillTileM - 1) / kPrefillTileM;
+    for (int i = 0; i < n; ++i) {
+      int32_t* t = tiles + 4 * (s_nt[e] + i);
+      t[0] = e;
+      t[1] = s_off[e] + i * kPrefillTileM;
+      t[2] = min(kPrefillTileM, s_cnt[e] - i * kPrefillTileM);
+      t[3] = 0;
+    }
+  }
+  int nsh = 0;
+  if (n_shared) {
+    nsh = (T + kPrefillTileM - 1) / kPrefillTileM;
+    for (int i = tid; i < nsh; i += blockDim.x) {
+      int32_t* t = tiles + 4 * (ntiles + i);
+      t[0] = -1;
+      t[1] = T * k + i * kPrefillTileM;
+      t[2] = min(kPrefillTileM, T - i * kPrefillTileM);
+      t[3] = 0;
+    }
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    ctrl[0] = ntiles + nsh;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, int T, int E,
+                                                 int k, const int32_t* __restrict__ blkbase,
+                                                 const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ lrank,
+                                                 int32_t* __restrict__ perm_tok,
+                                                 int32_t* __restrict__ inv_row) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= T * k) return;
+  const int e = ids[r];
+  const int t = r / k;
+  const int b = t / kHistTokensPerBlock;
+  const int pos = offsets[e] + blkbase[(size_t)b * E + e] + lrank[r];
+  perm_tok[pos] = t;
+  inv_row[r] = pos;
+}
+
+// ------------------------------------------------------------------ launch
+int launch_route_generic(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
+                         moe_routing* R, uint8_t* ws, const PrefillWs& P, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int E = L->n_experts, k = L->top_k, d = L->d;
+  if (!(flags & MOE_LOGITS_GIVEN)) {
+    dim3 grid((E + 3) / 4, (T + 7) / 8);
+    hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
+                       L->router_bias, R->logits, 1, (uint16_t*)nullptr, (uint16_t*)nullptr);
+  }
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, R->logits, T, E, k, R->topk_ids,
+                     R->topk_w);
+  int32_t* hist = (int32_t*)(ws + P.hist);
+  int32_t* lrank = (int32_t*)(ws + P.lrank);
+  hipLaunchKernelGGL(k_hist, dim3(P.nblk), dim3(256), 0, s, R->topk_ids, T, E, k, hist, lrank);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, P.nblk, E, T, k, L->n_shared,
+                     R->counts, R->offsets, (int32_t*)(ws + P.tiles), (int32_t*)(ws + P.ctrl));
+  hipLaunchKernelGGL(k_scatter, dim3((T * k + 255) / 256), dim3(256), 0, s, R->topk_ids, T, E, k,
+                     hist, R->offsets, lrank, R->perm_tok, R->inv_row);
+  return (int)hipGetLastError();
+}
+
+// decode routing: logits + staging, then select (2 launches)
+int launch_decode_route(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
+                        moe_routing* R, uint8_t* ws, const DecodeWs& W, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int E = L->n_experts, k = L->top_k, d = L->d;
+  const int do_logits = !(flags & MOE_LOGITS_GIVEN);
+  dim3 grid(max((E + 3) / 4, 64), 1);
+  hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
+                     L->router_bias, R->logits, do_logits, (uint16_t*)(ws + W.xs),
+                     (uint16_t*)(ws + W.xsum));
+  hipLaunchKernelGGL(k_dec_select, dim3(1), dim3(512), 0, s, R->logits, T, E, k, L->n_shared,
+                     R->topk_ids, R->topk_w, R->counts, R->offsets, R->perm_tok, R->inv_row,
+                     (int32_t*)(ws + W.slots), (uint32_t*)(ws + W.counters), d / 64);
+  return (int)hipGetLastError();
+}
+
+}  // namespace bqmoe

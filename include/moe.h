@@ -1,0 +1,172 @@
+/*
+ * moe.h -- C ABI of libbqmoe.so, a quantized mixture-of-experts expert layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes.  The pages on the Xolotl engine ("Xolotl"
+ * repository card, README section "How it works, in one paragraph") describe
+ * the idea: a mixture-of-experts model runs only the few experts each token's
+ * router asks for.  Their "Quick start" section names the expert weights'
+ * code families (mixed ternary / 2-bit / 3-bit) and "Fast mode" says decode
+ * speed is set by the expert bytes moved per token.  The pages give no
+ * formula; this library's definition is:
+ *
+ *   logits[t][e] = fp32( sum_i x[t][i] * Wr[e][i] + bias[e] )
+ *   ids[t][0..k)  = the k largest logits, descending, lower index first on ties
+ *   w[t][j]       = softmax over the k selected logits (fp32, sums to 1)
+ *   for each selected expert e and the shared expert (weight 1):
+ *       h = bf16( SiLU(x.Wg_e) * (x.Wu_e) ),   y_e = bf16( h.Wd_e )
+ *   out[t] = bf16( [x[t]] + sum_j w[t][j] * y_{ids[t][j]}[t] + y_shared[t] )
+ *
+ * Weights: W[k][n] = fp16 scale[n][k/32] * (level[n][k] - offset), with
+ * ternary levels 0..2 (offset 1: values -1, 0, +1), 2-bit levels 0..3
+ * (offset 1.5: -1.5 .. +1.5) and 3-bit levels 0..7 (offset 3.5: -3.5 .. +3.5).
+ * Products and sums are fp32 on the GPU; h, y and out are rounded to bf16.
+ *
+ * Conventions for every call below
+ *   - bf16 and fp16 values travel as uint16_t bit patterns.
+ *   - Device pointers are HIP device addresses; the caller owns and allocates
+ *     every buffer (inputs, outputs and the workspace).  The library allocates
+ *     nothing, keeps no pointer after returning and has no mutable global
+ *     state; calls are thread-safe.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *     on it and return without synchronising; argument errors are returned
+ *     before anything is enqueued.  A failed launch returns MOE_ERR_DEVICE.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - T == 0 is a no-op returning MOE_OK.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs (no floating-point atomics).
+ */
+#ifndef BQMOE_MOE_H
+#define BQMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, bad range, aliasing, misalignment */
+  MOE_ERR_UNSUPPORTED = 2, /* shape outside what the kernels handle */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_BAD_CODES = 4,   /* a level index outside its alphabet (moe_pack_weights) */
+  MOE_ERR_DEVICE = 5       /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_Q_TERNARY = 1, MOE_Q_INT2 = 2, MOE_Q_INT3 = 3 } moe_qtype;
+
+enum {
+  MOE_LOGITS_GIVEN = 1u, /* routing->logits is an input; the router matrix is not used */
+  MOE_ADD_RESIDUAL = 2u  /* out = x + MoE(x) */
+};
+
+/* Limits of this implementation (anything else returns MOE_ERR_UNSUPPORTED). */
+enum {
+  MOE_MAX_EXPERTS = 1024,
+  MOE_MAX_TOPK = 32,
+  MOE_MAX_DECODE_TOKENS = 8,
+  MOE_MAX_DIM = 65536 /* d and inter: multiples of 128 up to this */
+};
+
+/* ------------------------------------------------------------ packed format
+ * Packed format v1 of one projection W[K][N] (K % 128 == 0, N % 16 == 0).
+ * NT = N/16 n-tiles, KB = K/128 k-blocks.  For code (n, k): r = n%16,
+ * kk = k%128, gb = kk/32, j = kk%32, q = j/8, s = j%8, lane chunk L = 16q + r.
+ *   plane 0 (level & 3): tile (n/16, k/128) at ((n/16)*KB + k/128)*512 B;
+ *     chunk L at L*8 holds two little-endian 32-bit words; the code sits in
+ *     word gb/2 at bit 16*(s%2) + 2*(4*(gb%2) + s/2).
+ *   plane 1 (3-bit only, level >> 2): from the next 256-B boundary, 256 B
+ *     per tile, chunk L is one 32-bit word at L*4, bit 16*(s%2) + 4*gb + s/2.
+ *   scales: from the next 256-B boundary, 128 B per (n-tile, k-block) block,
+ *     fp16 scale[16*nt + r][4*kb + gb] at index r*4 + gb.
+ *   The size is rounded up to a multiple of 256 B.
+ * Each lane chunk of a tile is exactly what one lane of a 64-wide wavefront
+ * needs for a 16 x 32 bf16 matrix-core operand, so a wave reads a tile as
+ * one coalesced 512-B request.
+ */
+
+/* Bytes of one packed projection, or 0 if (qtype, K, N) is not supported. */
+size_t moe_packed_bytes(int qtype, int64_t K, int64_t N);
+
+/* Bytes of one packed expert: gate (K=d, N=inter), then up (same shape), then
+ * down (K=inter, N=d), each starting at a 256-B aligned offset.  0 if invalid. */
+size_t moe_expert_bytes(int q_gate, int q_up, int q_down, int64_t d, int64_t inter);
+
+/* Pack one projection on the host.
+ *   codes  : host, [N][K] level indices (row n holds k = 0..K-1)
+ *   scales : host, [N][K/32] fp16 bit patterns
+ *   out    : host buffer of out_bytes >= moe_packed_bytes(qtype, K, N); the
+ *            caller copies it to device memory.
+ * Returns MOE_ERR_UNSUPPORTED for a bad shape or qtype, MOE_ERR_BAD_CODES if
+ * a level is outside the alphabet (e.g. 3 in a ternary matrix), and
+ * MOE_ERR_INVALID_ARG for null pointers or a short buffer. */
+moe_status moe_pack_weights(int qtype, int64_t K, int64_t N, const uint8_t* codes,
+                            const uint16_t* scales, void* out, size_t out_bytes);
+
+/* ------------------------------------------------------------------ layer */
+typedef struct {
+  int32_t d;          /* hidden size, multiple of 128 */
+  int32_t inter;      /* expert intermediate size, multiple of 128 */
+  int32_t n_experts;  /* routed experts E, 1..1024 */
+  int32_t top_k;      /* k, 1..min(E, 32) */
+  int32_t n_shared;   /* 0 or 1 shared expert (weight 1, every token) */
+  int32_t q_gate, q_up, q_down; /* moe_qtype of each projection (shared expert too) */
+  const float* router_w;    /* device fp32 [E][d] (row e = expert e's router column);
+                               may be NULL only with MOE_LOGITS_GIVEN */
+  const float* router_bias; /* device fp32 [E] added to the logits, or NULL */
+  const void* experts;      /* device: expert e's packed blob at experts + e*expert_stride,
+                               256-B aligned (gate | up | down, see moe_expert_bytes) */
+  size_t expert_stride;     /* >= moe_expert_bytes(...), multiple of 256 */
+  const void* shared;       /* device packed shared expert (same layout), or NULL if none */
+} moe_layer;
+
+typedef struct {           /* caller-allocated device buffers, written by the calls below */
+  float* logits;           /* [T][E]; an input under MOE_LOGITS_GIVEN */
+  int32_t* topk_ids;       /* [T][k] */
+  float* topk_w;           /* [T][k] */
+  int32_t* counts;         /* [E] rows routed to each expert (shared expert not counted) */
+  int32_t* offsets;        /* [E+1] exclusive prefix sum of counts; offsets[E] == T*k */
+  int32_t* perm_tok;       /* [T*k] token of permuted row r (rows grouped by expert, tokens
+                              ascending within an expert) */
+  int32_t* inv_row;        /* [T][k] permuted row of (t, j) */
+} moe_routing;
+
+/* Device workspace needed by moe_route_topk / moe_forward_decode /
+ * moe_forward_prefill for T tokens (the largest of the three).  0 if the
+ * layer description is invalid. */
+size_t moe_workspace_bytes(const moe_layer* L, int32_t T);
+
+/* Router, top-k, weights and permutation only (the first steps of the layer).
+ *   x   : device bf16 [T][d] (ignored under MOE_LOGITS_GIVEN)
+ *   R   : all fields required; logits is written unless MOE_LOGITS_GIVEN
+ *   ws  : device workspace of ws_bytes >= moe_workspace_bytes(L, T) */
+moe_status moe_route_topk(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                          moe_routing* R, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer for 1..8 tokens (decode), bandwidth-bound kernels that
+ * stream each selected expert's packed bytes once for all its tokens.
+ *   x   : device bf16 [T][d];  out : device bf16 [T][d], must not overlap x
+ *   R   : routing outputs as in moe_route_topk
+ * T outside 1..8 returns MOE_ERR_INVALID_ARG. */
+moe_status moe_forward_decode(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                              moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out,
+                              void* stream);
+
+/* The whole layer for any T >= 1 (prefill): matrix-core grouped GEMMs over
+ * the permuted rows.  Arguments as for moe_forward_decode. */
+moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                               moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out,
+                               void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* ABI version of this header: 1. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BQMOE_MOE_H */

@@ -291,9 +291,12 @@ static void project(int qtype, int64_t K, int64_t N, const uint8_t* codes, const
     double acc = 0.0;
     const uint8_t* cn = codes + n * K;
     const uint16_t* sn = scales + n * (K / 32);
-    for (int64_t k = 0; k < K; ++k) {
-      double wkn = oracle_f16_to_f64(sn[k / 32]) * ((double)cn[k] - off);
-      acc += x[k] * wkn;
+    for (int64_t g = 0; g < K / 32; ++g) {
+      const double s = oracle_f16_to_f64(sn[g]); /* the group's scale */
+      for (int64_t k = g * 32; k < g * 32 + 32; ++k) {
+        double wkn = s * ((double)cn[k] - off);
+        acc += x[k] * wkn;
+      }
     }
     y[n] = acc;
   }

@@ -1,0 +1,87 @@
+"""Helpers for the GPU parity tests: run the oracle on the experts a set of
+tokens actually uses (regenerating only those experts), and the parity metrics.
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+import oracle
+import synth
+
+# Tolerance on floating-point outputs: both must hold for every output tensor.
+MAX_ERR_FRAC = 2e-2   # max |gpu - ref| <= 2e-2 * max |ref|
+REL_L1 = 1e-3         # sum |gpu - ref| / sum |ref| <= 1e-3
+
+
+def parity_stats(gpu_bf16: np.ndarray, ref_bf16: np.ndarray):
+    g = oracle.bf16_to_f64(gpu_bf16)
+    r = oracle.bf16_to_f64(ref_bf16)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    err = np.abs(g - r)
+    ref_max = float(np.abs(r).max()) or 1.0
+    return dict(max_err_frac=float(err.max()) / ref_max,
+                rel_l1=float(err.sum()) / max(float(np.abs(r).sum()), 1e-300),
+                frac_equal=float(np.mean(gpu_bf16 == ref_bf16)))
+
+
+def assert_parity(gpu_bf16, ref_bf16, what=""):
+    st = parity_stats(gpu_bf16, ref_bf16)
+    print(f"  parity {what}: {st}", flush=True)
+    assert st["max_err_frac"] <= MAX_ERR_FRAC, (what, st)
+    assert st["rel_l1"] <= REL_L1, (what, st)
+    return st
+
+
+def check_routing_exact(cfg, logits, gpu, tokens=None):
+    """ids, weights, counts, offsets, perm, inv_row of the GPU against the oracle run on the
+    same fp32 logits.  Integer results must be identical; weights within 2 fp32 ulp-ish."""
+    ids, w = oracle.topk_softmax(logits, cfg.k)
+    counts, offsets, perm_tok, inv_row = oracle.permute(ids, cfg.E)
+    assert np.array_equal(gpu["ids"], ids), "top-k ids differ"
+    assert np.array_equal(gpu["counts"], counts), "counts differ"
+    assert np.array_equal(gpu["offsets"], offsets), "offsets differ"
+    assert np.array_equal(gpu["perm_tok"][: ids.size], perm_tok), "perm_tok differs"
+    assert np.array_equal(gpu["inv_row"], inv_row), "inv_row differs"
+    assert np.allclose(gpu["w"], w, rtol=2e-6, atol=1e-7), "weights differ"
+    return ids, w, counts, offsets, perm_tok, inv_row
+
+
+def oracle_outputs(cfg, layer, x, logits, tokens, residual, seed=None, threads=8):
+    """Oracle output rows for `tokens` (bf16 [len(tokens)][d]).
+
+    Routing comes from the oracle on `logits`; only the experts the tokens use
+    are regenerated and evaluated.  Tokens are independent given their routing.
+    """
+    tokens = np.asarray(tokens)
+    ids, w = oracle.topk_softmax(logits[tokens], cfg.k)
+    n = len(tokens)
+    by_expert = {}
+    for i in range(n):
+        for j in range(cfg.k):
+            by_expert.setdefault(int(ids[i, j]), []).append((i, j))
+    y = np.zeros((n * cfg.k, cfg.d), np.uint16)
+    inv = np.zeros((n, cfg.k), np.int32)
+    ysh = np.zeros((n, cfg.d), np.uint16) if cfg.n_shared else None
+    xs = x[tokens]
+
+    def run(e):
+        mats = [synth.gen_matrix(cfg, layer, e, m, seed) for m in range(3)]
+        if e == cfg.E:
+            _, yy = oracle.expert_rows(cfg.qtypes, mats, xs)
+            return e, None, yy
+        rows = by_expert[e]
+        _, yy = oracle.expert_rows(cfg.qtypes, mats, xs[[i for i, _ in rows]])
+        return e, rows, yy
+
+    work = list(by_expert) + ([cfg.E] if cfg.n_shared else [])
+    with ThreadPoolExecutor(threads) as ex:
+        for e, rows, yy in ex.map(run, work):
+            if rows is None:
+                ysh[:] = yy
+            else:
+                for (i, j), yrow in zip(rows, yy):
+                    y[i * cfg.k + j] = yrow
+                    inv[i, j] = i * cfg.k + j
+    return oracle.combine(w, inv, y, ysh, xs, residual)

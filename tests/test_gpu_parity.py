@@ -1,0 +1,278 @@
+"""GPU parity tests: the HIP path through the C ABI against the CPU oracle.
+
+Integer results (top-k ids, counts, offsets, permutation, inverse map) must be
+bit-exact; floating-point outputs must satisfy max|err| <= 2e-2 * max|ref| and
+sum|err| / sum|ref| <= 1e-3.  Routing is checked by running the oracle on the
+fp32 logits the GPU used, so that both sides take the integer decisions on
+the same values; the GPU's own logits are checked against the oracle's
+double-precision logits separately.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_moe_router_amd as bq
+import oracle
+import synth
+import workloads
+from helpers import assert_parity, check_routing_exact, oracle_outputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _to_dev_u16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def _host_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def _routing_host(R, T, k):
+    return dict(ids=R.topk_ids.cpu().numpy(), w=R.topk_w.cpu().numpy(),
+                counts=R.counts.cpu().numpy(), offsets=R.offsets.cpu().numpy(),
+                perm_tok=R.perm_tok.cpu().numpy()[: T * k], inv_row=R.inv_row.cpu().numpy(),
+                logits=R.logits.cpu().numpy())
+
+
+def _run(dl, x_np, mode, flags=0, logits=None):
+    cfg = dl.cfg
+    T = x_np.shape[0]
+    x = _to_dev_u16(x_np)
+    lg = None if logits is None else torch.from_numpy(np.ascontiguousarray(logits)).to(DEV)
+    R = bq.alloc_routing(T, cfg.E, cfg.k, DEV, logits=lg)
+    if logits is not None:
+        flags |= bq.MOE_LOGITS_GIVEN
+    ws = bq.alloc_workspace(dl.handle, T, DEV)
+    out = torch.empty((T, cfg.d), dtype=torch.int16, device=DEV)
+    fn = bq.moe_forward_decode if mode == "decode" else bq.moe_forward_prefill
+    fn(dl.handle, x, T, flags, R, ws, out)
+    torch.cuda.synchronize()
+    return _host_u16(out), _routing_host(R, T, cfg.k)
+
+
+def _full_check(dl, x, mode, flags=0, logits=None, label=""):
+    cfg = dl.cfg
+    print(f"[{label}] {mode} T={x.shape[0]} cfg={cfg.name}", flush=True)
+    out, rt = _run(dl, x, mode, flags, logits)
+    if logits is None:
+        ref_logits = oracle.router_logits(x, synth.gen_router(cfg), synth.gen_bias(cfg))
+        assert_parity_f32(rt["logits"], ref_logits)
+        used = rt["logits"]
+    else:
+        used = logits
+        assert np.array_equal(rt["logits"], logits)
+    check_routing_exact(cfg, used, rt)
+    tokens = np.arange(x.shape[0])
+    ref = oracle_outputs(cfg, dl.layer, x, used, tokens, bool(flags & bq.MOE_ADD_RESIDUAL))
+    assert_parity(out, ref, f"{label} out")
+    return out, rt
+
+
+def assert_parity_f32(gpu, ref):
+    err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+    assert err.max() <= 2e-2 * np.abs(ref).max()
+    assert err.sum() <= 1e-3 * np.abs(ref).sum()
+
+
+@pytest.fixture(scope="module")
+def layers():
+    cache = {}
+
+    def get(name, cfg=None):
+        if name not in cache:
+            cfg = cfg or synth.CONFIGS[name]
+            print(f"building layer {name} ({cfg.name})", flush=True)
+            cache[name] = workloads.DeviceLayer(cfg, 0, DEV)
+        return cache[name]
+
+    yield get
+    cache.clear()
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ tiny
+def test_c0_decode(layers):
+    dl = layers("c0")
+    _full_check(dl, synth.gen_x(dl.cfg), "decode", label="c0")
+
+
+def test_c0_prefill(layers):
+    dl = layers("c0")
+    out_p, _ = _full_check(dl, synth.gen_x(dl.cfg), "prefill", label="c0")
+    out_d, _ = _run(dl, synth.gen_x(dl.cfg), "decode")
+    # both paths compute the same layer; they may differ by bf16 rounding of near-ties only
+    assert_parity(out_p, out_d, "c0 prefill vs decode")
+
+
+def test_c0_route_topk_matches_oracle(layers):
+    dl = layers("c0")
+    cfg = dl.cfg
+    x = synth.gen_x(cfg)
+    R = bq.alloc_routing(cfg.T, cfg.E, cfg.k, DEV)
+    ws = bq.alloc_workspace(dl.handle, cfg.T, DEV)
+    bq.moe_route_topk(dl.handle, _to_dev_u16(x), cfg.T, 0, R, ws)
+    torch.cuda.synchronize()
+    rt = _routing_host(R, cfg.T, cfg.k)
+    check_routing_exact(cfg, rt["logits"], rt)
+
+
+# ------------------------------------------------------------ multi-tile
+MULTI = synth.small_config(synth.CONFIGS["c3"], name="multitile", T=700, d=512, E=16, k=4,
+                           inter=256, router=False, zipf_s=0.0)
+
+
+def test_prefill_multitile_ragged(layers):
+    dl = layers("multitile", MULTI)
+    x = synth.gen_x(MULTI)
+    logits = synth.gen_logits(MULTI)
+    _full_check(dl, x, "prefill", logits=logits, label="multitile")
+
+
+def test_prefill_multitile_residual_and_skew(layers):
+    cfg = synth.small_config(MULTI, name="multitile_skew", zipf_s=1.2, residual=True,
+                             q_gate=synth.QT_TERNARY, q_up=synth.QT_TERNARY,
+                             q_down=synth.QT_TERNARY, T=513)
+    dl = layers("multitile_skew", cfg)
+    x = synth.gen_x(cfg)
+    logits = synth.gen_logits(cfg)
+    _full_check(dl, x, "prefill", flags=bq.MOE_ADD_RESIDUAL, logits=logits, label="skew")
+
+
+def test_prefill_int3_mixed(layers):
+    cfg = synth.small_config(MULTI, name="int3mix", q_gate=synth.QT_INT3, q_up=synth.QT_INT2,
+                             q_down=synth.QT_INT3, T=300)
+    dl = layers("int3mix", cfg)
+    _full_check(dl, synth.gen_x(cfg), "prefill", logits=synth.gen_logits(cfg), label="int3mix")
+    _full_check(dl, synth.gen_x(cfg, T=8), "decode", logits=synth.gen_logits(cfg, T=8),
+                label="int3mix")
+
+
+# ------------------------------------------------------------- full size
+def test_c1_decode_full(layers):
+    dl = layers("c1")
+    _full_check(dl, synth.gen_x(dl.cfg), "decode", label="c1")
+
+
+def test_c2_decode_full(layers):
+    dl = layers("c2")
+    out, rt = _full_check(dl, synth.gen_x(dl.cfg), "decode", label="c2")
+    U = int((rt["counts"] > 0).sum())
+    print(f"  c2 unique routed experts U={U}", flush=True)
+
+
+def test_decode_is_deterministic(layers):
+    dl = layers("c2")
+    x = synth.gen_x(dl.cfg)
+    a, _ = _run(dl, x, "decode")
+    b, _ = _run(dl, x, "decode")
+    assert np.array_equal(a, b)
+
+
+def test_c3_prefill_full_sampled(layers):
+    dl = layers("c3")
+    cfg = dl.cfg
+    x = synth.gen_x(cfg)
+    logits = synth.gen_logits(cfg)
+    print("[c3] prefill T=8192", flush=True)
+    out, rt = _run(dl, x, "prefill", logits=logits)
+    ids, *_ = check_routing_exact(cfg, logits, rt)
+    counts = rt["counts"]
+    hot = int(np.argmax(counts))
+    cold = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    toks = {0, cfg.T - 1, 1, cfg.T // 2}
+    toks |= set(np.where((ids == hot).any(1))[0][:3].tolist())
+    toks |= set(np.where((ids == cold).any(1))[0][:3].tolist())
+    toks = np.array(sorted(toks))
+    ref = oracle_outputs(cfg, 0, x, logits, toks, False)
+    assert_parity(out[toks], ref, "c3 sampled out")
+
+
+def test_c4_stack_full_sampled(layers):
+    cfg = synth.CONFIGS["c4"]
+    x = synth.gen_x(cfg)
+    for layer in range(cfg.layers):
+        print(f"[c4] building layer {layer}", flush=True)
+        dl = workloads.DeviceLayer(cfg, layer, DEV)
+        logits = synth.gen_logits(cfg, layer)
+        out, rt = _run(dl, x, "prefill", flags=bq.MOE_ADD_RESIDUAL, logits=logits)
+        ids, *_ = check_routing_exact(cfg, logits, rt)
+        counts = rt["counts"]
+        print(f"  layer {layer}: max rows/expert {counts.max()}, empty experts "
+              f"{int((counts == 0).sum())}", flush=True)
+        hot = int(np.argmax(counts))
+        toks = {0, cfg.T - 1, 7}
+        toks |= set(np.where((ids == hot).any(1))[0][-2:].tolist())
+        nz = np.where(counts > 0)[0]
+        rare = int(nz[np.argmin(counts[nz])])
+        toks |= set(np.where((ids == rare).any(1))[0][:2].tolist())
+        toks = np.array(sorted(toks))
+        # per-layer check: the oracle gets this layer's GPU input
+        ref = oracle_outputs(cfg, layer, x, logits, toks, True)
+        assert_parity(out[toks], ref, f"c4 layer {layer} sampled out")
+        x = out  # next layer's input
+        del dl
+        torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ edge cases
+def test_ties_and_k_equals_E(layers):
+    cfg = synth.small_config(synth.CONFIGS["c0"], name="ties", E=8, k=8, T=6, router=False)
+    dl = layers("ties", cfg)
+    x = synth.gen_x(cfg)
+    logits = np.zeros((cfg.T, cfg.E), np.float32)
+    logits[1] = [1, 1, 0.5, 1, -0.0, 0.0, 1, 2]
+    logits[2] = np.float32(1e-45) * np.arange(8)
+    logits[3] = -np.arange(8, dtype=np.float32)
+    logits[4] = [3, 3, 3, 3, 3, 3, 3, 3]
+    logits[5] = [0.0, -0.0, 0.0, -0.0, 1, 1, 1, 1]
+    for mode in ("decode", "prefill"):
+        _full_check(dl, x, mode, logits=logits, label=f"ties-{mode}")
+
+
+def test_single_expert_top1(layers):
+    cfg = synth.small_config(synth.CONFIGS["c0"], name="e1", E=1, k=1, T=5, router=False,
+                             n_shared=1)
+    dl = layers("e1", cfg)
+    logits = np.zeros((cfg.T, 1), np.float32)
+    _full_check(dl, synth.gen_x(cfg), "decode", logits=logits, label="e1")
+    _full_check(dl, synth.gen_x(cfg), "prefill", logits=logits, label="e1")
+
+
+def test_all_tokens_one_expert_decode(layers):
+    dl = layers("c1")
+    cfg = dl.cfg
+    T = 8
+    x = synth.gen_x(cfg, T=T)
+    logits = np.tile(np.linspace(1, -1, cfg.E, dtype=np.float32), (T, 1))
+    _full_check(dl, x, "decode", logits=logits, label="one-hot-experts")
+
+
+def test_zero_weights_give_shared_only(layers):
+    cfg = synth.small_config(synth.CONFIGS["c0"], name="zero", n_shared=1,
+                             q_gate=synth.QT_TERNARY, q_up=synth.QT_TERNARY,
+                             q_down=synth.QT_TERNARY, router=False)
+
+    def zero_routed(host, stride):
+        # every routed expert's codes at level 1 (weight 0); scales untouched
+        for e in range(cfg.E):
+            blob = workloads.pack_expert(cfg, 0, e)
+            off = 0
+            for m in range(3):
+                K, N = synth.matrix_shape(cfg, m)
+                c, s = synth.gen_matrix(cfg, 0, e, m)
+                nb = bq.moe_packed_bytes(cfg.qtypes[m], K, N)
+                bq.moe_pack_weights(cfg.qtypes[m], np.ones_like(c), s, blob[off:off + nb])
+                off += nb
+            host[e * stride:(e + 1) * stride] = blob
+
+    dl = workloads.DeviceLayer(cfg, 0, DEV, experts_override=zero_routed)
+    x = synth.gen_x(cfg)
+    logits = synth.gen_logits(cfg)
+    for mode in ("decode", "prefill"):
+        out, _ = _run(dl, x, mode, logits=logits)
+        mats = [synth.gen_matrix(cfg, 0, cfg.E, m) for m in range(3)]
+        _, ysh = oracle.expert_rows(cfg.qtypes, mats, x)
+        assert_parity(out, ysh, f"zero-{mode}")

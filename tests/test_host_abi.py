@@ -1,0 +1,185 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/moe.h declares;
+* the host packer agrees with the oracle's independent decoder of the format
+  (both written from the format definition) on every level and on special
+  scales;
+* every argument error is reported with its status code before any launch.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_quantized_moe_router_amd as bq
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bq.load()
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+    assert declared == set(bq.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert bq.moe_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(6):
+        assert bq.status_string(s) and bq.status_string(s) != "unknown status"
+
+
+@pytest.mark.parametrize("q,K,N", [(1, 128, 16), (2, 256, 128), (3, 128, 256), (2, 4096, 2048),
+                                   (3, 2048, 4096), (2, 100, 16), (2, 128, 8), (0, 128, 16)])
+def test_packed_bytes_matches_oracle(q, K, N):
+    assert bq.moe_packed_bytes(q, K, N) == oracle.packed_bytes(q, K, N)
+
+
+def test_expert_bytes():
+    assert bq.moe_expert_bytes(2, 2, 2, 4096, 2048) == 7_864_320
+    assert bq.moe_expert_bytes(3, 3, 2, 4096, 2048) == 9_961_472
+    assert bq.moe_expert_bytes(1, 1, 1, 4096, 2048) == 7_864_320
+    assert bq.moe_expert_bytes(2, 2, 2, 256, 128) == 30_720
+    assert bq.moe_expert_bytes(2, 2, 2, 100, 128) == 0
+
+
+@pytest.mark.parametrize("q", [1, 2, 3])
+@pytest.mark.parametrize("K,N", [(128, 16), (256, 48), (384, 32)])
+def test_pack_then_oracle_unpack_is_identity(q, K, N):
+    levels = synth.LEVELS[q]
+    codes = synth.codes(11, q, N * K, levels).reshape(N, K)
+    codes[0, :] = np.arange(K) % levels  # every level at every position class
+    scales = synth.absnormal_f16(11, 100 + q, N * K // 32, 0.05).reshape(N, K // 32)
+    special = np.uint16([0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0xFBFF, 0x3C00, 0xBC00])
+    scales.reshape(-1)[:special.size] = special
+    blob = bq.moe_pack_weights(q, codes, scales)
+    assert blob.nbytes == oracle.packed_bytes(q, K, N)
+    c2, s2 = oracle.unpack(q, K, N, blob)
+    assert np.array_equal(c2, codes)
+    assert np.array_equal(s2, scales)
+
+
+def test_pack_exhaustive_single_positions():
+    # each (level, k-slot) of one 16 x 128 tile placed alone decodes to itself
+    K, N = 128, 16
+    for q in (2, 3):
+        for k in range(K):
+            for u in range(1, synth.LEVELS[q]):
+                codes = np.zeros((N, K), np.uint8)
+                codes[(k * 7) % N, k] = u
+                blob = bq.moe_pack_weights(q, codes, np.zeros((N, 4), np.uint16))
+                c2, _ = oracle.unpack(q, K, N, blob)
+                assert np.array_equal(c2, codes), (q, k, u)
+
+
+def test_pack_rejects_bad_input():
+    lib = bq.load()
+    codes = np.zeros((16, 128), np.uint8)
+    scales = np.zeros((16, 4), np.uint16)
+    out = np.zeros(bq.moe_packed_bytes(1, 128, 16), np.uint8)
+    codes[3, 5] = 3  # not a ternary level
+    with pytest.raises(bq.MoeError) as ei:
+        bq.moe_pack_weights(1, codes, scales, out)
+    assert ei.value.status == bq.MOE_ERR_BAD_CODES
+    codes[3, 5] = 8
+    with pytest.raises(bq.MoeError) as ei:
+        bq.moe_pack_weights(3, codes, scales)
+    assert ei.value.status == bq.MOE_ERR_BAD_CODES
+    codes[3, 5] = 0
+    st = lib.moe_pack_weights(2, 128, 16, codes.ctypes.data, scales.ctypes.data,
+                              out.ctypes.data, out.nbytes - 1)
+    assert st == bq.MOE_ERR_INVALID_ARG
+    st = lib.moe_pack_weights(2, 100, 16, codes.ctypes.data, scales.ctypes.data,
+                              out.ctypes.data, out.nbytes)
+    assert st == bq.MOE_ERR_UNSUPPORTED
+    st = lib.moe_pack_weights(2, 128, 16, None, scales.ctypes.data, out.ctypes.data, out.nbytes)
+    assert st == bq.MOE_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- validation
+FAKE = 1 << 40  # a 256-aligned address that is never dereferenced: every call below fails first
+
+
+def _layer(**kw):
+    p = dict(d=256, inter=128, n_experts=8, top_k=2, n_shared=0, qtypes=(2, 2, 2),
+             experts=FAKE, expert_stride=30_720, shared=None, router_w=FAKE, router_bias=None)
+    p.update(kw)
+    return bq.make_layer(p["d"], p["inter"], p["n_experts"], p["top_k"], p["n_shared"],
+                         p["qtypes"], p["experts"], p["expert_stride"], p["shared"],
+                         p["router_w"], p["router_bias"])
+
+
+def _routing():
+    return bq.moe_routing(*([FAKE] * 7))
+
+
+def _call(fn, L, T, flags=0, R=None, ws=FAKE, ws_bytes=None, x=FAKE, out=FAKE + (1 << 30)):
+    lib = bq.load()
+    R = _routing() if R is None else R
+    if ws_bytes is None:
+        ws_bytes = max(1, lib.moe_workspace_bytes(ctypes.byref(L.c), T))
+    f = getattr(lib, fn)
+    args = [ctypes.byref(L.c), x, T, flags, ctypes.byref(R), ws, ws_bytes]
+    if fn != "moe_route_topk":
+        args.append(out)
+    args.append(None)
+    return f(*args)
+
+
+@pytest.mark.parametrize("fn", ["moe_forward_decode", "moe_forward_prefill", "moe_route_topk"])
+def test_argument_errors_return_status(fn):
+    L = _layer()
+    assert _call(fn, L, -1) == bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, L, 2, flags=0x80) == bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, _layer(d=100), 2) == bq.MOE_ERR_UNSUPPORTED
+    assert _call(fn, _layer(inter=200), 2) == bq.MOE_ERR_UNSUPPORTED
+    assert _call(fn, _layer(qtypes=(2, 5, 2)), 2) == bq.MOE_ERR_UNSUPPORTED
+    assert _call(fn, _layer(n_experts=2000, top_k=2), 2) == bq.MOE_ERR_UNSUPPORTED
+    assert _call(fn, _layer(top_k=9), 2) == bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, _layer(n_shared=2), 2) == bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, _layer(router_w=None), 2) == bq.MOE_ERR_INVALID_ARG
+    R = _routing()
+    R.perm_tok = None
+    assert _call(fn, L, 2, R=R) == bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, L, 2, ws_bytes=10) == bq.MOE_ERR_WORKSPACE
+    assert _call(fn, L, 2, ws=None) == bq.MOE_ERR_WORKSPACE
+    assert _call(fn, L, 2, ws=FAKE + 8) == bq.MOE_ERR_INVALID_ARG
+    if fn != "moe_route_topk":
+        assert _call(fn, _layer(expert_stride=30_720 - 256), 2) == bq.MOE_ERR_INVALID_ARG
+        assert _call(fn, _layer(expert_stride=30_720 + 8), 2) == bq.MOE_ERR_INVALID_ARG
+        assert _call(fn, _layer(experts=FAKE + 16), 2) == bq.MOE_ERR_INVALID_ARG
+        assert _call(fn, _layer(n_shared=1, shared=None), 2) == bq.MOE_ERR_INVALID_ARG
+        assert _call(fn, L, 2, out=FAKE + 256) == bq.MOE_ERR_INVALID_ARG  # overlaps x
+        assert _call(fn, L, 2, out=None) == bq.MOE_ERR_INVALID_ARG
+        assert _call(fn, L, 2, x=FAKE + 2) == bq.MOE_ERR_INVALID_ARG
+
+
+def test_decode_token_range():
+    L = _layer()
+    assert _call("moe_forward_decode", L, 0) == bq.MOE_ERR_INVALID_ARG
+    assert _call("moe_forward_decode", L, 9) == bq.MOE_ERR_INVALID_ARG
+    # 8 tokens x top-9 = 72 routed rows exceeds the decode kernels' 64
+    L9 = _layer(n_experts=16, top_k=9)
+    assert _call("moe_forward_decode", L9, 8) == bq.MOE_ERR_UNSUPPORTED
+
+
+def test_zero_tokens_is_a_noop():
+    L = _layer()
+    assert _call("moe_forward_prefill", L, 0) == bq.MOE_OK
+    assert _call("moe_route_topk", L, 0) == bq.MOE_OK
+
+
+def test_workspace_bytes():
+    lib = bq.load()
+    L = _layer()
+    sizes = [lib.moe_workspace_bytes(ctypes.byref(L.c), T) for T in (1, 4, 8, 9, 100, 1000)]
+    assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
+    assert lib.moe_workspace_bytes(ctypes.byref(_layer(d=100).c), 4) == 0
+    assert lib.moe_workspace_bytes(ctypes.byref(L.c), -1) == 0

@@ -1,0 +1,73 @@
+"""Device-resident synthetic layers for the tests, the smoke check and the benchmark.
+
+Glue only: draws the canonical inputs from ``synth`` (seeded, counter-based),
+packs each projection with the library's own host packer
+(``moe_pack_weights``) and uploads the blobs with torch.  Holds none of the
+layer's arithmetic.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import bit_quantized_moe_router_amd as bq
+import synth
+
+
+def host_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def pack_expert(cfg: synth.Config, layer: int, e: int, out: np.ndarray | None = None,
+                seed: int | None = None) -> np.ndarray:
+    """Packed gate|up|down blob of expert e (e == E is the shared expert)."""
+    nbytes = bq.moe_expert_bytes(*cfg.qtypes, cfg.d, cfg.inter)
+    if out is None:
+        out = np.empty(nbytes, np.uint8)
+    off = 0
+    for m in range(3):
+        K, N = synth.matrix_shape(cfg, m)
+        c, s = synth.gen_matrix(cfg, layer, e, m, seed)
+        nb = bq.moe_packed_bytes(cfg.qtypes[m], K, N)
+        bq.moe_pack_weights(cfg.qtypes[m], c, s, out[off:off + nb])
+        off += nb
+    return out
+
+
+class DeviceLayer:
+    """One layer's packed experts (+ shared expert, router, bias) in device memory."""
+
+    def __init__(self, cfg: synth.Config, layer: int = 0, device="cuda", seed=None,
+                 experts_override=None):
+        self.cfg = cfg
+        self.layer = layer
+        E = cfg.E
+        self.stride = bq.moe_expert_bytes(*cfg.qtypes, cfg.d, cfg.inter)
+        host = np.empty(E * self.stride, np.uint8)
+
+        def work(e):
+            pack_expert(cfg, layer, e, host[e * self.stride:(e + 1) * self.stride], seed)
+
+        with ThreadPoolExecutor(host_threads()) as ex:
+            list(ex.map(work, range(E)))
+        if experts_override is not None:
+            experts_override(host, self.stride)
+        self.experts = torch.from_numpy(host).to(device)
+        self.shared = None
+        if cfg.n_shared:
+            sh = pack_expert(cfg, layer, E, None, seed)
+            self.shared = torch.from_numpy(sh).to(device)
+        self.router_w = None
+        if cfg.router:
+            self.router_w = torch.from_numpy(synth.gen_router(cfg, layer, seed)).to(device)
+        b = synth.gen_bias(cfg, layer, seed) if cfg.router else None
+        self.router_bias = None if b is None else torch.from_numpy(b).to(device)
+        self.handle = self.make_handle(self.experts, self.shared)
+
+    def make_handle(self, experts: torch.Tensor, shared: torch.Tensor | None) -> bq.Layer:
+        c = self.cfg
+        return bq.make_layer(c.d, c.inter, c.E, c.k, c.n_shared, c.qtypes, experts, self.stride,
+                             shared, self.router_w, self.router_bias)
