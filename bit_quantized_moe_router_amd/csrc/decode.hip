@@ -12,7 +12,8 @@
 //   B = packed levels turned into the bf16 value 128 + 16u by one shift, one
 //       mask and one or per pair of levels (see device_common.h),
 //   C = -(8 + offset) * (sum of the group's activations), produced by a
-//       16x16x16 op from the activation sums staged in three bf16 parts,
+//       second 16x16x32 op (zero-padded) from the activation sums staged in
+//       three bf16 parts,
 // so D is exactly sum_k x * (u - offset) for one 32-group; it is scaled by the
 // group's fp16 scale and accumulated in fp32.  Partial sums of the waves meet
 // in LDS in a fixed order (deterministic, no floating-point atomics).
@@ -138,11 +139,10 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_gateup(
 #pragma unroll
     for (int i = 0; i < MAXKB; ++i) {
       if (kbase + i < kb1) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #define BQ_GU_STEP(GB)                                                                \
   {                                                                                   \
-    const f32x4 cgc = mfma16(ac[i][GB], bcg, z);                                      \
-    const f32x4 cuc = (QG3 == QU3 && cg == cu) ? cgc : mfma16(ac[i][GB], bcu, z);     \
+    const f32x4 cgc = mfma_corr(ac[i][GB], bcg);                                      \
+    const f32x4 cuc = (QG3 == QU3 && cg == cu) ? cgc : mfma_corr(ac[i][GB], bcu);     \
     group_step<QG3, GB>(ag[0], ax[i][GB], wg[i][0], hg[i][0], sg[i][0], cgc);          \
     group_step<QG3, GB>(ag[1], ax[i][GB], wg[i][1], hg[i][1], sg[i][1], cgc);          \
     group_step<QU3, GB>(au[0], ax[i][GB], wu[i][0], hu[i][0], su[i][0], cuc);          \
@@ -263,10 +263,9 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_down(
 #pragma unroll
     for (int i = 0; i < MAXKB; ++i) {
       if (kbase + i < kb1) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #define BQ_DN_STEP(GB)                                                        \
   {                                                                           \
-    const f32x4 cc = mfma16(ac[i][GB], bc, z);                                \
+    const f32x4 cc = mfma_corr(ac[i][GB], bc);                                \
     _Pragma("unroll") for (int j = 0; j < NTW; ++j)                           \
         group_step<QD3, GB>(acc[j], ax[i][GB], wd[i][j], hd[i][j], sd[i][j], cc); \
   }

@@ -39,10 +39,14 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-// 16x16x16 bf16: lane l supplies A[l%16][4(l/16)..+3], B[4(l/16)..+3][l%16].
-__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
-                                                   __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+// Correction term of one 32-group as a 16x16x32 op (same shape as the main op,
+// so the main op can take it as its C operand without a mixed-shape dependency):
+// lanes 0..15 put the row's bf16 triple (-hi, -mid, -lo, 0) in k-slots 0..3 of A
+// and (c, c, c, 0) in k-slots 0..3 of B; every other slot is zero.  Result:
+// D[row][col] = -c * (hi + mid + lo)[row] for every column.
+__device__ __forceinline__ f32x4 mfma_corr(u32x2 a, u32x2 b) {
+  const u32x4 a4 = {a[0], a[1], 0u, 0u}, b4 = {b[0], b[1], 0u, 0u};
+  return mfma32(a4, b4, f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
 // ---------------------------------------------------------- code unpacking

@@ -68,7 +68,7 @@ struct PrefillWs {
 };
 
 constexpr int kHistTokensPerBlock = 256;  // tokens per histogram block
-constexpr int kPrefillTileM = 128;        // rows per grouped-GEMM tile
+constexpr int kPrefillTileM = 64;         // rows per grouped-GEMM tile
 
 DecodeWs decode_ws_layout(const moe_layer* L, int T);
 PrefillWs prefill_ws_layout(const moe_layer* L, int T);

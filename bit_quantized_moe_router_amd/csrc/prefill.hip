@@ -11,8 +11,8 @@
 //   - each wave reads its packed tiles straight from global memory: a tile's
 //     lane chunk is exactly the lane's B operand, so no LDS is needed for B;
 //     levels become the bf16 value 128 + 16u with a shift, a mask and an or;
-//   - per 32-group: C = -(8 + offset) * sum(x) by a 16x16x16 op, D = A*B + C by
-//     16x16x32 ops, acc += scale * D in fp32.
+//   - per 32-group: C = -(8 + offset) * sum(x) by a zero-padded 16x16x32 op,
+//     D = A*B + C by 16x16x32 ops, acc += scale * D in fp32.
 // Epilogues: gate/up -> h = bf16(SiLU(g) * u), stored as h/16 with the 32-group
 // sums of h for the down projection; down -> y = bf16(acc).
 #include <hip/hip_runtime.h>
@@ -22,8 +22,8 @@
 
 namespace bqmoe {
 
-constexpr int kRows = kPrefillTileM;  // 128
-constexpr int kRowStride = 136;       // bf16 per LDS row (128 + 8 pad)
+constexpr int kRows = kPrefillTileM;  // rows per tile = 16 * RT
+constexpr int RT = kRows / 16;        // 16-row tiles per wave
 
 __device__ __forceinline__ float silu_pf(float g) { return g / (1.0f + expf(-g)); }
 
@@ -71,12 +71,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // NMAT = 2: gate and up (NTPW n-tiles of each per wave); NMAT = 1: down (NTPW n-tiles).
 //
-// LDS per buffer: 16 chunk columns x 128 rows x 16 B of activations (chunk c of
-// row R at c*2048 + R*16: the 16 rows a matrix-core read touches are 256
+// LDS per buffer: 16 chunk columns x kRows rows x 16 B of activations (chunk c
+// of row R at c*kRows*16 + R*16: the 16 rows a matrix-core read touches are 256
 // contiguous bytes, and every address is one base register plus an immediate),
-// then 128 rows x 32 B of group sums.  Both are filled with direct global->LDS
-// loads, which need no registers.
+// then kRows rows x 32 B of group sums.  Both are filled with direct
+// global->LDS loads (64 lanes x 16 B = 64 rows of one chunk column per
+// instruction), which need no registers.
+constexpr int kColBytes = kRows * 16;
 constexpr int kBufBytes = kRows * 256 + kRows * 32;
+constexpr int kDmaA = 16 * kRows / 64;   // activation DMA instructions per k-block
+constexpr int kDmaS = kRows * 32 / 1024; // group-sum DMA instructions per k-block
+static_assert(kRows % 64 == 0 && kDmaA % 4 == 0, "tile rows");
 
 template <int NMAT, int NTPW, bool Q3A, bool Q3B, bool SAMEC>
 __global__ __launch_bounds__(256, 2) void k_pf_gemm(
@@ -104,10 +109,12 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
   }
   __syncthreads();
 
-  // per-lane source rows of the direct-to-LDS loads: rows lane and 64 + lane
-  const uint16_t* arow0 = A + (size_t)sTok[lane] * K;
-  const uint16_t* arow1 = A + (size_t)sTok[64 + lane] * K;
-  const uint16_t* srow = Asum + ((size_t)sTok[wave * 32 + (lane >> 1)] * G + (lane & 1) * 2) * 4;
+  // per-lane source rows of the direct-to-LDS loads: rows 64*h + lane
+  const uint16_t* arow[kRows / 64];
+#pragma unroll
+  for (int h = 0; h < kRows / 64; ++h) arow[h] = A + (size_t)sTok[64 * h + lane] * K;
+  const int s_wave_row = (wave < kDmaS ? wave : 0) * 32 + (lane >> 1);
+  const uint16_t* srow = Asum + ((size_t)sTok[s_wave_row] * G + (lane & 1) * 2) * 4;
 
   // this wave's streams: stream j -> projection (j / NTPW), n-tile nt0 + j % NTPW
   const int nt0 = (blockIdx.y * 4 + wave) * NTPW;
@@ -122,9 +129,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
     bc1[1] = f32_to_bf16(cb);
   }
 
-  f32x4 acc[8][4];
+  f32x4 acc[RT][4];
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -134,15 +141,21 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
 #define BQ_ISSUE(KB_, BUF_)                                                                    \
   {                                                                                            \
     uint8_t* dst = sbuf + (BUF_) * kBufBytes;                                                  \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                            \
-      const int ci = wave * 8 + i; /* chunk column ci/2, rows 64*(ci%2).. */                  \
-      const uint16_t* src = ((ci & 1) ? arow1 : arow0) + (KB_) * 128 + (ci >> 1) * 8;          \
+    _Pragma("unroll") for (int i = 0; i < kDmaA / 4; ++i) {                                    \
+      const int ci = wave * (kDmaA / 4) + i; /* column ci / RH, rows 64 * (ci % RH) .. */      \
+      constexpr int RH = kRows / 64;                                                           \
+      const uint16_t* src = arow[ci % RH] + (KB_) * 128 + (ci / RH) * 8;                       \
       __builtin_amdgcn_global_load_lds((const void*)src,                                       \
-                                       (lds_void*)(dst + (ci >> 1) * 2048 + (ci & 1) * 1024),  \
+                                       (lds_void*)(dst + (ci / RH) * kColBytes + (ci % RH) * 1024), \
                                        16, 0, 0);                                              \
     }                                                                                          \
-    __builtin_amdgcn_global_load_lds((const void*)(srow + (KB_) * 16),                         \
-                                     (lds_void*)(dst + kRows * 256 + wave * 1024), 16, 0, 0);  \
+    if (wave < kDmaS)                                                                          \
+      __builtin_amdgcn_global_load_lds((const void*)(srow + (KB_) * 16),                       \
+                                       (lds_void*)(dst + kRows * 256 + wave * 1024), 16, 0, 0); \
+  }
+
+#define BQ_LOADB(KB_)                                                                          \
+  {                                                                                            \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                            \
       const bool first = (j / NTPW == 0);                                                      \
       const uint8_t* bb = first ? base0 : base1;                                               \
@@ -159,16 +172,12 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
   BQ_ISSUE(0, 0)
   for (int kb = 0; kb < KB; ++kb) {
     const int buf = kb & 1;
+    BQ_LOADB(kb)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // k-block kb is in LDS for every wave; buffer buf^1 is free
-    u32x2 cw[4], cs[4];
-    uint32_t chh[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      cw[j] = pw[j];
-      cs[j] = ps[j];
-      chh[j] = ph[j];
-    }
+    const u32x2* cw = pw;
+    const u32x2* cs = ps;
+    const uint32_t* chh = ph;
     if (kb + 1 < KB) BQ_ISSUE(kb + 1, buf ^ 1)
     const uint8_t* sA = sbuf + buf * kBufBytes;
     const uint8_t* sS = sA + kRows * 256;
@@ -183,14 +192,14 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
       const uint32_t sbits = ((GB < 2) ? cs[j][0] : cs[j][1]) >> (16 * (GB & 1));               \
       sc[j] = f16_to_f32(sbits & 0xFFFFu);                                                      \
     }                                                                                           \
-    _Pragma("unroll") for (int rt = 0; rt < 8; ++rt) {                                          \
+    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                         \
       const uint2 sv = *reinterpret_cast<const uint2*>(sS + (rt * 16 + r) * 32 + GB * 8);      \
       const u32x2 av = {q == 0 ? sv.x : 0u, q == 0 ? sv.y : 0u};                                \
-      const f32x4 corr0 = mfma16(av, bc0, f32x4{0.f, 0.f, 0.f, 0.f});                           \
+      const f32x4 corr0 = mfma_corr(av, bc0);                           \
       f32x4 corr1 = corr0;                                                                      \
-      if constexpr (!SAMEC) corr1 = mfma16(av, bc1, f32x4{0.f, 0.f, 0.f, 0.f});               \
+      if constexpr (!SAMEC) corr1 = mfma_corr(av, bc1);               \
       const u32x4 a =                                                                           \
-          *reinterpret_cast<const u32x4*>(sA + (GB * 4 + q) * 2048 + (rt * 16 + r) * 16);       \
+          *reinterpret_cast<const u32x4*>(sA + (GB * 4 + q) * kColBytes + (rt * 16 + r) * 16);  \
       _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                           \
         const f32x4 dd = mfma32(a, b[j], (j / NTPW == 0) ? corr0 : corr1);                      \
         acc[rt][j][0] = fmaf(sc[j], dd[0], acc[rt][j][0]);                                      \
@@ -211,6 +220,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
 #undef BQ_PF_GROUP
   }
 #undef BQ_ISSUE
+#undef BQ_LOADB
 
   // ------------------------------------------------------------ epilogues
   if constexpr (NMAT == 2) {
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
     // the wave's 2*16 = 32 columns form one 32-group of the down projection
     const int I = N;
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = rt * 16 + 4 * q + i;
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
     }
   } else {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = rt * 16 + 4 * q + i;
