@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized MoE expert layer on one MI355X.
+
+Default run (prints one JSON line):
+  * decode, 1 token (256 experts top-8 + shared, d=4096, I=2048, 2-bit group-32
+    weights): one step = one full layer call (router, top-k, permutation,
+    gate/up + SiLU, down + weighted combine).  Each step uses a fresh token and
+    the next of 8 device copies of the layer (16 GB), so no step finds its
+    expert bytes in the 256 MB Infinity Cache.  The K timed steps are one HIP
+    graph; `value` is packed expert bytes per step / step time (GB/s).
+  * roofline: the gate/up kernel (two thirds of the streamed bytes) timed
+    launch by launch with HIP events on its stream.
+  * prefill, 8192 tokens (logits given): tokens/s of the full layer call and
+    the grouped GEMMs' matrix-core utilisation (useful flops / GEMM time /
+    2.5 PFLOP/s).
+  * cpu_baseline: the CPU oracle on a bounded sample of decode tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized MoE layer: decode µs/layer + HBM GB/s; prefill tokens/s + MFMA %"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["bit_quantized_moe_router_amd/csrc/decode.hip",
+                  "bit_quantized_moe_router_amd/csrc/device_common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the rocprofv3 counter runs, if taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c1", choices=["c1", "c2"], help="decode workload")
+    ap.add_argument("--copies", type=int, default=8, help="device copies of the layer to rotate")
+    ap.add_argument("--prefill-config", default="c3", choices=["c3", "c4", "none"])
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--kernel-loop", type=int, default=0,
+                    help="profiling aid: only launch the decode gate/up stage this many times")
+    return ap.parse_args()
+
+
+def decode_leg(args, dev):
+    import numpy as np
+    import torch
+
+    import bit_quantized_moe_router_amd as bq
+    import synth
+    import workloads
+
+    cfg = synth.CONFIGS[args.config]
+    T, K, W, C = cfg.T, args.steps, args.warmup, max(1, args.copies)
+    log(f"[decode] building {cfg.name} + {C - 1} device copies")
+    base = workloads.DeviceLayer(cfg, 0, dev)
+    experts = [base.experts] + [base.experts.clone() for _ in range(C - 1)]
+    shared = [base.shared] + [None if base.shared is None else base.shared.clone()
+                              for _ in range(C - 1)]
+    handles = [base.make_handle(e, s) for e, s in zip(experts, shared)]
+    n = W + K
+    X = synth.gen_x(cfg, T=T * n).reshape(n, T, cfg.d)
+    xd = torch.from_numpy(X.view(np.int16)).to(dev)
+    R = bq.alloc_routing(T, cfg.E, cfg.k, dev)
+    ws = bq.alloc_workspace(handles[0], T, dev)
+    out = torch.empty((T, cfg.d), dtype=torch.int16, device=dev)
+    ebytes = bq.moe_expert_bytes(*cfg.qtypes, cfg.d, cfg.inter)
+    router_bytes = cfg.E * cfg.d * 4 if cfg.router else 0
+
+    def step(i):
+        bq.moe_forward_decode(handles[i % C], xd[i], T, 0, R, ws, out)
+
+    # bytes streamed per step: each active expert (and the shared one) once
+    active = []
+    for i in range(W, n):
+        step(i)
+        active.append(int((R.counts > 0).sum().item()) + cfg.n_shared)
+    torch.cuda.synchronize()
+    bytes_per_step = float(np.mean(active)) * ebytes
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # eager timing (includes host launch overhead)
+    t0 = time.perf_counter()
+    for i in range(W, n):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / K
+
+    # the K timed steps as one HIP graph
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(W, n):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+
+    # dominant kernel: gate/up, one launch per prepared workspace (layer copy j, token j)
+    wss = [bq.alloc_workspace(handles[0], T, dev) for _ in range(C)]
+    Rs = [bq.alloc_routing(T, cfg.E, cfg.k, dev) for _ in range(C)]
+    outs = [torch.empty((T, cfg.d), dtype=torch.int16, device=dev) for _ in range(C)]
+    gu_bytes = []
+    for j in range(C):
+        bq.moe_forward_decode(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j])
+        gu_bytes.append((int((Rs[j].counts > 0).sum().item()) + cfg.n_shared) *
+                        (bq.moe_packed_bytes(cfg.q_gate, cfg.d, cfg.inter) +
+                         bq.moe_packed_bytes(cfg.q_up, cfg.d, cfg.inter)))
+    torch.cuda.synchronize()
+    GU = bq.MOE_DECODE_STAGE_GATEUP
+    if args.kernel_loop:
+        for r in range(args.kernel_loop):
+            j = r % C
+            bq.moe_forward_decode_stages(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j], GU)
+        torch.cuda.synchronize()
+        return None
+    reps = max(K, 8 * C)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for r in range(reps):
+        j = r % C
+        evs[r][0].record()
+        bq.moe_forward_decode_stages(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j], GU)
+        evs[r][1].record()
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3  # us
+    gu_us = float(np.mean(durs))
+    gu_b = float(np.mean([gu_bytes[r % C] for r in range(reps)]))
+    traffic = measured_traffic("k_dec_gateup")
+    roof = {"kernel": "k_dec_gateup (decode gate/up + SiLU)", "bound": "hbm",
+            "achieved": gu_b / (gu_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+            "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_b}
+    res = dict(cfg=cfg, ms=ms, eager_ms=eager_ms, bytes_per_step=bytes_per_step,
+               router_bytes=router_bytes, roof=roof, active=float(np.mean(active)))
+    del g, experts, shared, handles
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_leg(args, dev):
+    import numpy as np
+    import torch
+
+    import bit_quantized_moe_router_amd as bq
+    import synth
+    import workloads
+
+    cfg = synth.CONFIGS[args.prefill_config]
+    T = cfg.T
+    log(f"[prefill] building {cfg.name}")
+    layers = [workloads.DeviceLayer(cfg, l, dev) for l in range(cfg.layers)]
+    x = torch.from_numpy(synth.gen_x(cfg).view(np.int16)).to(dev)
+    bufs = [x, torch.empty_like(x)]
+    Rs = [bq.alloc_routing(T, cfg.E, cfg.k, dev,
+                           logits=torch.from_numpy(synth.gen_logits(cfg, l)).to(dev))
+          for l in range(cfg.layers)]
+    ws = bq.alloc_workspace(layers[0].handle, T, dev)
+    flags = bq.MOE_LOGITS_GIVEN | (bq.MOE_ADD_RESIDUAL if cfg.residual else 0)
+
+    def stack(mask=bq.MOE_PREFILL_STAGES_ALL, events=None):
+        for l, dl in enumerate(layers):
+            src, dst = bufs[l % 2], bufs[(l + 1) % 2]
+            if events is not None:
+                events[l][0].record()
+            bq.moe_forward_prefill_stages(dl.handle, src, T, flags, Rs[l], ws, dst, mask)
+            if events is not None:
+                events[l][1].record()
+
+    stack()
+    torch.cuda.synchronize()
+    K = max(1, args.prefill_steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        stack()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_stack = e0.elapsed_time(e1) / K
+    # grouped-GEMM time per layer: run each layer's preparation, then time its GEMM stages
+    gemm_ms = []
+    rows = []
+    for l, dl in enumerate(layers):
+        src, dst = bufs[l % 2], bufs[(l + 1) % 2]
+        prep = bq.MOE_PREFILL_STAGE_ROUTE | bq.MOE_PREFILL_STAGE_STAGE_X
+        bq.moe_forward_prefill_stages(dl.handle, src, T, flags, Rs[l], ws, dst, prep)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        for r in range(K):
+            ev[r][0].record()
+            bq.moe_forward_prefill_stages(dl.handle, src, T, flags, Rs[l], ws, dst,
+                                          bq.MOE_PREFILL_STAGE_GATEUP | bq.MOE_PREFILL_STAGE_DOWN)
+            ev[r][1].record()
+        torch.cuda.synchronize()
+        gemm_ms.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
+        rows.append(int(Rs[l].counts.sum().item()) + T * cfg.n_shared)
+    flops = sum(2.0 * r * 3 * cfg.d * cfg.inter for r in rows)
+    gemm_total_ms = float(sum(gemm_ms))
+    res = {"workload": cfg.name, "T": T, "layers": cfg.layers,
+           "ms_per_stack": ms_stack, "ms_per_layer": ms_stack / cfg.layers,
+           "tokens_per_s": T / (ms_stack * 1e-3),
+           "tokens_per_s_per_layer": T * cfg.layers / (ms_stack * 1e-3),
+           "gemm_ms_per_layer": gemm_ms, "useful_tflop_per_stack": flops / 1e12,
+           "mfma_frac": flops / (gemm_total_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+           "mfma_frac_whole_layer": flops / (ms_stack * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args, cfg, bytes_per_step):
+    """The CPU oracle (single-threaded C, double precision) on a bounded token sample."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    budget = args.cpu_seconds
+    Wr = synth.gen_router(cfg) if cfg.router else None
+    bias = synth.gen_bias(cfg)
+    X = synth.gen_x(cfg, T=64 * cfg.T, seed=cfg.seed + 1000).reshape(64, cfg.T, cfg.d)
+    spent, done = 0.0, 0
+    while done < 64 and (spent < budget or done < 2):
+        x = X[done]
+        mats = {}
+        L = oracle.router_logits(x, Wr, bias)
+        ids, w = oracle.topk_softmax(L, cfg.k)
+        need = sorted(set(ids.reshape(-1).tolist())) + ([cfg.E] if cfg.n_shared else [])
+        for e in need:  # regenerating the weights is not part of the timed work
+            mats[e] = [synth.gen_matrix(cfg, 0, e, m) for m in range(3)]
+        t0 = time.perf_counter()
+        L = oracle.router_logits(x, Wr, bias)
+        ids, w = oracle.topk_softmax(L, cfg.k)
+        counts, offsets, perm, inv = oracle.permute(ids, cfg.E)
+        y = np.zeros((cfg.T * cfg.k, cfg.d), np.uint16)
+        for e in range(cfg.E):
+            if counts[e]:
+                rows = perm[offsets[e]:offsets[e + 1]]
+                _, y[offsets[e]:offsets[e + 1]] = oracle.expert_rows(cfg.qtypes, mats[e], x[rows])
+        ysh = oracle.expert_rows(cfg.qtypes, mats[cfg.E], x)[1] if cfg.n_shared else None
+        oracle.combine(w, inv, y, ysh, x, False)
+        spent += time.perf_counter() - t0
+        done += 1
+    per_step = spent / done
+    return {"value": bytes_per_step / per_step / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} decode steps of {cfg.name} (T={cfg.T}) through the full CPU oracle "
+                      f"(logits, top-k, permutation, every active expert + shared, combine), "
+                      f"single-threaded C in double precision; {per_step * 1e3:.0f} ms per step; "
+                      f"weight regeneration excluded",
+            "ms_per_step": per_step * 1e3, "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the whole layer (all experts) fits in one MI355X's HBM "
+              "and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    import bit_quantized_moe_router_amd as bq
+
+    bq.load()
+    d = decode_leg(args, dev)
+    if d is None:  # profiling loop only
+        return
+    pre = None if args.prefill_config == "none" else prefill_leg(args, dev)
+    cfg = d["cfg"]
+    cpu = cpu_baseline(args, cfg, d["bytes_per_step"]) if args.cpu_seconds > 0 else None
+    gbs = d["bytes_per_step"] / (d["ms"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": d["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "experts": cfg.E, "top_k": cfg.k,
+                   "shared": cfg.n_shared, "inter": cfg.inter,
+                   "quant": [synth_qname(q) for q in cfg.qtypes], "layer_copies": args.copies,
+                   "step": "one full decode layer call (fresh token, next layer copy)"},
+        "us_per_layer": d["ms"] * 1e3,
+        "us_per_layer_eager": d["eager_ms"] * 1e3,
+        "packed_expert_bytes_per_step": d["bytes_per_step"],
+        "active_experts_per_step": d["active"],
+        "gbs_incl_router": (d["bytes_per_step"] + d["router_bytes"]) / (d["ms"] * 1e-3) / 1e9,
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "roofline": d["roof"],
+        "cpu_baseline": cpu,
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def synth_qname(q):
+    return {1: "ternary", 2: "int2", 3: "int3"}[q]
+
+
+if __name__ == "__main__":
+    main()

@@ -22,9 +22,16 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_BAD
 MOE_Q_TERNARY, MOE_Q_INT2, MOE_Q_INT3 = 1, 2, 3
 MOE_LOGITS_GIVEN, MOE_ADD_RESIDUAL = 1, 2
 MOE_MAX_DECODE_TOKENS = 8
+MOE_DECODE_STAGE_ROUTE, MOE_DECODE_STAGE_SELECT, MOE_DECODE_STAGE_GATEUP, MOE_DECODE_STAGE_DOWN = \
+    1, 2, 4, 8
+MOE_DECODE_STAGES_ALL = 15
+MOE_PREFILL_STAGE_ROUTE, MOE_PREFILL_STAGE_STAGE_X, MOE_PREFILL_STAGE_GATEUP, \
+    MOE_PREFILL_STAGE_DOWN, MOE_PREFILL_STAGE_COMBINE = 1, 2, 4, 8, 16
+MOE_PREFILL_STAGES_ALL = 31
 
 EXPORTED = ("moe_packed_bytes", "moe_expert_bytes", "moe_pack_weights", "moe_workspace_bytes",
-            "moe_route_topk", "moe_forward_decode", "moe_forward_prefill", "moe_status_string",
+            "moe_route_topk", "moe_forward_decode", "moe_forward_prefill",
+            "moe_forward_decode_stages", "moe_forward_prefill_stages", "moe_status_string",
             "moe_abi_version")
 
 
@@ -74,7 +81,10 @@ def load():
     lib.moe_route_topk.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp]
     lib.moe_forward_decode.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, vp]
     lib.moe_forward_prefill.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, vp]
-    for f in (lib.moe_route_topk, lib.moe_forward_decode, lib.moe_forward_prefill):
+    lib.moe_forward_decode_stages.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, u32, vp]
+    lib.moe_forward_prefill_stages.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, u32, vp]
+    for f in (lib.moe_route_topk, lib.moe_forward_decode, lib.moe_forward_prefill,
+              lib.moe_forward_decode_stages, lib.moe_forward_prefill_stages):
         f.restype = i32
     lib.moe_status_string.argtypes, lib.moe_status_string.restype = [i32], ctypes.c_char_p
     lib.moe_abi_version.argtypes, lib.moe_abi_version.restype = [], i32
@@ -209,6 +219,24 @@ def moe_forward_prefill(layer: Layer, x, T: int, flags: int, routing: Routing, w
                                     ctypes.byref(routing.c), _ptr(ws),
                                     0 if ws is None else ws.numel(), _ptr(out), _stream(stream))
     _check(st, "moe_forward_prefill")
+
+
+def moe_forward_decode_stages(layer: Layer, x, T: int, flags: int, routing: Routing, ws, out,
+                              stage_mask: int, stream=None):
+    st = load().moe_forward_decode_stages(ctypes.byref(layer.c), _ptr(x), T, flags,
+                                          ctypes.byref(routing.c), _ptr(ws),
+                                          0 if ws is None else ws.numel(), _ptr(out), stage_mask,
+                                          _stream(stream))
+    _check(st, "moe_forward_decode_stages")
+
+
+def moe_forward_prefill_stages(layer: Layer, x, T: int, flags: int, routing: Routing, ws, out,
+                               stage_mask: int, stream=None):
+    st = load().moe_forward_prefill_stages(ctypes.byref(layer.c), _ptr(x), T, flags,
+                                           ctypes.byref(routing.c), _ptr(ws),
+                                           0 if ws is None else ws.numel(), _ptr(out),
+                                           stage_mask, _stream(stream))
+    _check(st, "moe_forward_prefill_stages")
 
 
 def moe_abi_version() -> int:

@@ -21,13 +21,25 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, src + ".o")
+# The decode kernels keep matrix-core results in ordinary vector registers:
+# their epilogue per op is a single multiply-add, which would otherwise need
+# an extra accumulator-register read each.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def compile_command(src: str, out: str, device_asm: bool = False) -> list:
+    """hipcc command line for one source (an object file, or device assembly)."""
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", f"--offload-arch={ARCH}", *COMMON, "-c", path, "-o", obj]
-    else:
-        cmd = [HIPCC, "-x", "c++", *COMMON, "-c", path, "-o", obj]
+        mode = ["--cuda-device-only", "-S"] if device_asm else ["-c"]
+        return [HIPCC, "-x", "hip", f"--offload-arch={ARCH}", *COMMON, *EXTRA.get(src, []),
+                *mode, path, "-o", out]
+    return [HIPCC, "-x", "c++", *COMMON, "-c", path, "-o", out]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = compile_command(src, obj)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

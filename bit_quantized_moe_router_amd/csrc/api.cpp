@@ -28,17 +28,15 @@ DecodeWs decode_ws_layout(const moe_layer* L, int T) {
   w.rows = T * k + T * S;
   size_t o = 0;
   w.slots = o;
-  o = al256(o + sizeof(int32_t) * (1 + 3 * (size_t)w.max_slots));
-  w.counters = o;
-  o = al256(o + sizeof(uint32_t) * (size_t)(d / 64));
+  o = al256(o + sizeof(int32_t) * kSlotRec * (1 + (size_t)w.max_slots));
   w.xs = o;
   o = al256(o + 2 * (size_t)T * d);
   w.xsum = o;
-  o = al256(o + 8 * (size_t)T * (d / 32));
+  o = al256(o + 16 * (size_t)T * (d / 32));
   w.hs = o;
   o = al256(o + 2 * (size_t)w.rows * I);
   w.hsum = o;
-  o = al256(o + 8 * (size_t)w.rows * (I / 32));
+  o = al256(o + 16 * (size_t)w.rows * (I / 32));
   w.y = o;
   o = al256(o + 2 * (size_t)w.rows * d);
   w.total = o;
@@ -65,11 +63,11 @@ PrefillWs prefill_ws_layout(const moe_layer* L, int T) {
   p.xs = o;
   o = al256(o + 2 * (size_t)T * d);
   p.xsum = o;
-  o = al256(o + 8 * (size_t)T * (d / 32));
+  o = al256(o + 16 * (size_t)T * (d / 32));
   p.h = o;
   o = al256(o + 2 * (size_t)p.rows * I);
   p.hsum = o;
-  o = al256(o + 8 * (size_t)p.rows * (I / 32));
+  o = al256(o + 16 * (size_t)p.rows * (I / 32));
   p.y = o;
   o = al256(o + 2 * (size_t)p.rows * d);
   p.total = o;
@@ -143,24 +141,26 @@ extern "C" moe_status moe_route_topk(const moe_layer* L, const uint16_t* x, int3
                                                                          : MOE_OK;
 }
 
-extern "C" moe_status moe_forward_decode(const moe_layer* L, const uint16_t* x, int32_t T,
-                                         uint32_t flags, moe_routing* R, void* ws,
-                                         size_t ws_bytes, uint16_t* out, void* stream) {
+static moe_status decode_impl(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                              moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out,
+                              uint32_t mask, void* stream) {
   if (T < 1 || T > MOE_MAX_DECODE_TOKENS) return MOE_ERR_INVALID_ARG;
   moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, true);
   if (st != MOE_OK) return st;
-  if (T * L->top_k > kDecodeMaxRoutedRows || T * (L->top_k + L->n_shared) > kDecodeMaxRows)
+  if (T * L->top_k > kDecodeMaxRoutedRows || T * (L->top_k + L->n_shared) > kDecodeMaxRows ||
+      L->d > kDecodeMaxDim || L->inter > kDecodeMaxDim || !decode_shape_ok(L, T))
     return MOE_ERR_UNSUPPORTED;
   if (!out || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
   const size_t bytes = (size_t)T * L->d * 2;
   if (overlaps(x, bytes, out, bytes)) return MOE_ERR_INVALID_ARG;
   const DecodeWs W = decode_ws_layout(L, T);
-  return launch_decode(L, x, T, flags, R, (uint8_t*)ws, W, out, stream) ? MOE_ERR_DEVICE : MOE_OK;
+  return launch_decode(L, x, T, flags, R, (uint8_t*)ws, W, out, stream, mask) ? MOE_ERR_DEVICE
+                                                                            : MOE_OK;
 }
 
-extern "C" moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T,
-                                          uint32_t flags, moe_routing* R, void* ws,
-                                          size_t ws_bytes, uint16_t* out, void* stream) {
+static moe_status prefill_impl(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                               moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out,
+                               uint32_t mask, void* stream) {
   if (T == 0 && L && R) return MOE_OK;
   moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, true);
   if (st != MOE_OK) return st;
@@ -168,8 +168,36 @@ extern "C" moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x,
   const size_t bytes = (size_t)T * L->d * 2;
   if (overlaps(x, bytes, out, bytes)) return MOE_ERR_INVALID_ARG;
   const PrefillWs P = prefill_ws_layout(L, T);
-  return launch_prefill(L, x, T, flags, R, (uint8_t*)ws, P, out, stream) ? MOE_ERR_DEVICE
-                                                                        : MOE_OK;
+  return launch_prefill(L, x, T, flags, R, (uint8_t*)ws, P, out, stream, mask) ? MOE_ERR_DEVICE
+                                                                             : MOE_OK;
+}
+
+extern "C" moe_status moe_forward_decode(const moe_layer* L, const uint16_t* x, int32_t T,
+                                         uint32_t flags, moe_routing* R, void* ws,
+                                         size_t ws_bytes, uint16_t* out, void* stream) {
+  return decode_impl(L, x, T, flags, R, ws, ws_bytes, out, ~0u, stream);
+}
+
+extern "C" moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T,
+                                          uint32_t flags, moe_routing* R, void* ws,
+                                          size_t ws_bytes, uint16_t* out, void* stream) {
+  return prefill_impl(L, x, T, flags, R, ws, ws_bytes, out, ~0u, stream);
+}
+
+extern "C" moe_status moe_forward_decode_stages(const moe_layer* L, const uint16_t* x, int32_t T,
+                                                uint32_t flags, moe_routing* R, void* ws,
+                                                size_t ws_bytes, uint16_t* out,
+                                                uint32_t stage_mask, void* stream) {
+  if (stage_mask == 0 || (stage_mask & ~(uint32_t)MOE_DECODE_STAGES_ALL)) return MOE_ERR_INVALID_ARG;
+  return decode_impl(L, x, T, flags, R, ws, ws_bytes, out, stage_mask, stream);
+}
+
+extern "C" moe_status moe_forward_prefill_stages(const moe_layer* L, const uint16_t* x, int32_t T,
+                                                 uint32_t flags, moe_routing* R, void* ws,
+                                                 size_t ws_bytes, uint16_t* out,
+                                                 uint32_t stage_mask, void* stream) {
+  if (stage_mask == 0 || (stage_mask & ~(uint32_t)MOE_PREFILL_STAGES_ALL)) return MOE_ERR_INVALID_ARG;
+  return prefill_impl(L, x, T, flags, R, ws, ws_bytes, out, stage_mask, stream);
 }
 
 extern "C" const char* moe_status_string(moe_status s) {

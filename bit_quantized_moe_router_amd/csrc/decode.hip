@@ -1,320 +1,317 @@
 // Decode kernels (1..8 tokens): stream each selected expert's packed bytes
-// once for all of the tokens routed to it (the pages' "Latest" section of the
-// "Xolotl" README describes decoding an expert once for all its tokens; its
-// "Fast mode" section notes that decode speed is set by the expert bytes read
-// per token).
+// once for all of the tokens routed to it (the "Xolotl" README's "Latest"
+// section describes decoding an expert once for all its tokens; its "Fast
+// mode" section notes that decode speed is set by the expert bytes read per
+// token).
 //
-// Work unit: (slot, column group) where a slot is one active expert (or the
-// shared expert) with its M <= 16 rows.  A block's waves split the reduction
-// dimension into contiguous k-block ranges, issue every load of their range up
-// front, then run the 16x16x32 bf16 matrix-core op with
-//   A = activations / 16 of the slot's rows (rows beyond M are zero),
-//   B = packed levels turned into the bf16 value 128 + 16u by one shift, one
-//       mask and one or per pair of levels (see device_common.h),
-//   C = -(8 + offset) * (sum of the group's activations), produced by a
-//       second 16x16x32 op (zero-padded) from the activation sums staged in
-//       three bf16 parts,
-// so D is exactly sum_k x * (u - offset) for one 32-group; it is scaled by the
-// group's fp16 scale and accumulated in fp32.  Partial sums of the waves meet
-// in LDS in a fixed order (deterministic, no floating-point atomics).
+// One kernel template serves both projections.  A block is (slot, column
+// group): a slot is one active expert (or the shared expert) with its M <= 8
+// rows; the column group is one 16-column n-tile of gate and of up (2
+// streams), or 4 n-tiles (64 output columns) of down (4 streams).  The
+// block's waves split the reduction dimension into contiguous k-block ranges,
+// each wave owning 16 (stream, k-block) tiles.  A wave
+//   1. copies its slice of the slot's M activation rows (pre-scaled by 1/16)
+//      and of their 32-group sums from global memory straight into its own
+//      LDS region,
+//   2. issues the loads of all its packed tiles,
+//   3. waits for the copies only (loads complete in issue order), and
+//   4. works through its k-blocks as their tiles arrive; per 32-group:
+//        A = the rows from LDS (lanes of rows >= M read row 0; those outputs
+//            are discarded),
+//        B = packed levels turned into bf16 values base + 16u by one
+//            mask-and-or per pair of levels (see device_common.h),
+//        C = the group's correction term (see mfma_corr in device_common.h),
+//      so D = sum_k x * (u - offset) exactly for the group; D is scaled by the
+//      group's fp16 scale (2 bytes per lane, broadcast with a lane shuffle)
+//      and accumulated in fp32, only in the accumulator rows that hold real
+//      rows.
+// Partial sums of the waves meet in LDS in a fixed order: no floating-point
+// atomics, no cross-block synchronisation.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace bqmoe {
 
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-}
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kDecMaxRows = 8;  // rows of one slot (<= T <= 8)
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-// One 32-group step for one n-tile: D = A*B + C, acc += scale * D.
-template <bool Q3, int GB>
-__device__ __forceinline__ void group_step(f32x4& acc, u32x4 a, u32x2 w0, uint32_t w1, u32x2 sc,
-                                           f32x4 corr) {
-  const uint32_t word = (GB < 2) ? w0[0] : w0[1];
-  u32x4 b;
-  if constexpr (Q3)
-    b = unpack3<GB>(word, w1);
-  else
-    b = unpack2<GB & 1>(word);
-  const f32x4 dd = mfma32(a, b, corr);
-  const uint32_t sbits = ((GB < 2) ? sc[0] : sc[1]) >> (16 * (GB & 1));
-  const float s = f16_to_f32(sbits & 0xFFFFu);
-  acc[0] = fmaf(s, dd[0], acc[0]);
-  acc[1] = fmaf(s, dd[1], acc[1]);
-  acc[2] = fmaf(s, dd[2], acc[2]);
-  acc[3] = fmaf(s, dd[3], acc[3]);
+// Masks and bases of the 2-bit unpacking (see unpack2 in device_common.h),
+// passed as kernel arguments.  The masks stay in scalar registers and the
+// bases are copied once into vector registers (an identity lane move), so
+// that each mask-and-or is one v_and_or_b32: with literal constants, or with
+// both operands scalar, it would take two instructions (a VOP3 op here takes
+// no literal and at most one scalar operand).
+struct Unpack2K {
+  uint32_t m0, m1, m2, b0, b1, b2;
+};
+static const Unpack2K kUnpack2 = {0x00030003u, 0x000C000Cu, 0x00300030u,
+                                  0x45004500u, 0x44004400u, 0x43004300u};
+
+__device__ __forceinline__ uint32_t lane_copy(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, true);  // quad_perm 0,1,2,3
 }
 
-// Staged activation sums -> split sum in bf16 triple, (hi, mid, lo) negated.
-__device__ __forceinline__ uint2 split3_neg(float s) {
-  const uint32_t hi = f32_to_bf16(s);
-  const float r1 = s - bf16_to_f32(hi);
-  const uint32_t mid = f32_to_bf16(r1);
-  const float r2 = r1 - bf16_to_f32(mid);
-  const uint32_t lo = f32_to_bf16(r2);
-  uint2 v;
-  v.x = ((hi ^ 0x8000u) & 0xFFFFu) | (((mid ^ 0x8000u) & 0xFFFFu) << 16);
-  v.y = (lo ^ 0x8000u) & 0xFFFFu;
-  return v;
+struct Unpack2R {
+  uint32_t m0, m1, m2, b0, b1, b2;  // b* in vector registers
+};
+
+template <int P>
+__device__ __forceinline__ u32x4 unpack2_r(uint32_t w, const Unpack2R& c) {
+  const uint32_t x = P ? (w >> 8) : w;
+  u32x4 r;
+  r[0] = (x & c.m0) | c.b0;
+  r[1] = (x & c.m1) | c.b1;
+  r[2] = (x & c.m2) | c.b2;
+  r[3] = ((x >> 2) & c.m2) | c.b2;
+  return r;
 }
 
-// ------------------------------------------------------------ gate / up
-// Block = (slot, 32 intermediate columns = 2 n-tiles) for both gate and up.
-template <bool QG3, bool QU3, int KSPLIT, int MAXKB>
-__global__ __launch_bounds__(64 * KSPLIT) void k_dec_gateup(
+// LDS region of one wave: activation rows [M][KBW*128 bf16 + 16 B pad], then
+// staged sums [M][KBW*4][16 B]; each part rounded up to whole KB, as the
+// direct loads fill 1 KB per instruction.
+__host__ __device__ constexpr int dw_row_stride(int kbw) { return kbw * 256 + 16; }
+__host__ __device__ constexpr int dw_rows_bytes(int M, int kbw) {
+  return (M * dw_row_stride(kbw) + 1023) & ~1023;
+}
+__host__ __device__ constexpr int dw_sum_bytes(int M, int kbw) {
+  return (M * kbw * 64 + 1023) & ~1023;
+}
+__host__ __device__ constexpr int dw_bytes(int M, int kbw) {
+  return dw_rows_bytes(M, kbw) + dw_sum_bytes(M, kbw);
+}
+
+// GATEUP = true: streams 0 (gate) and 1 (up) of n-tile blockIdx % groups;
+//   epilogue h = bf16(SiLU(g) * u), stored as h/16, plus fp32 (W, S) sums of
+//   h over the tile's 16 columns (half of a 32-group of the down projection).
+// GATEUP = false (down): streams 0..3 = n-tiles 4g .. 4g+3; the 32-group sums
+//   of h are the two half sums added; epilogue y = bf16(acc).
+template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KSPLIT, int KBW>
+__global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
-    ProjDesc pg, ProjDesc pu, const int32_t* __restrict__ slots,
-    const int32_t* __restrict__ perm_tok, const uint16_t* __restrict__ xs,
-    const uint16_t* __restrict__ xsum, int d, int I, int Tk, float cg, float cu,
-    uint16_t* __restrict__ hs, uint16_t* __restrict__ hsum) {
-  __shared__ float red[KSPLIT][16][64];
-  __shared__ float hval[16][32];
-  const int groups = I / 32;
+    ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ slots, const uint16_t* __restrict__ A,
+    const uint8_t* __restrict__ Asum, int K, int N, int Mmax, float ca, float cb,
+    uint16_t* __restrict__ out, float* __restrict__ out_psum, Unpack2K uk) {
+  constexpr int NS = GATEUP ? 2 : 4;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int groups = N / (16 * (GATEUP ? 1 : 4));
   const int slot = blockIdx.x / groups, grp = blockIdx.x % groups;
   if (slot >= slots[0]) return;
-  const int e = slots[1 + 3 * slot], row0 = slots[2 + 3 * slot], M = slots[3 + 3 * slot];
+  // the slot record is uniform: scalar loads, which do not wait behind the
+  // packed-tile loads below
+  const int32_t* rec = slots + kSlotRec * (1 + slot);
+  const int e = rec[0], row0 = rec[1], M = rec[2];
+  int src_row[kDecMaxRows];
+#pragma unroll
+  for (int c = 0; c < kDecMaxRows; ++c)
+    src_row[c] = GATEUP ? (c < M ? rec[kSlotTok + c] : rec[kSlotTok]) : row0 + (c < M ? c : 0);
   const uint8_t* blob = e >= 0 ? experts + (size_t)e * stride : shared;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
-  const int KB = d / 128;
+  // projection offsets in registers before any LDS write (which the compiler
+  // cannot tell apart from the argument memory)
+  const uint8_t* code_base[2] = {blob + pa.off, blob + pb.off};
+  const size_t plane1[2] = {pa.plane1, pb.plane1};
+  const size_t scale_off[2] = {pa.scales, pb.scales};
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KB = K / 128, G = K / 32;
   const int per = (KB + KSPLIT - 1) / KSPLIT;
-  const int kb0 = min(KB, wave * per), kb1 = min(KB, kb0 + per);
-  const bool tok_ok = r < M;
-  const int row = row0 + r;
-  const int tok = tok_ok ? (row < Tk ? perm_tok[row] : row - Tk) : 0;
-  const uint16_t* xrow = xs + (size_t)tok * d;
-  const uint16_t* srow = xsum + (size_t)tok * (d / 32) * 4;
+  const int kb0 = min(KB, wave * per);
+  const int nkb = min(KB, kb0 + per) - kb0;  // 0 .. KBW
+  constexpr int RS = dw_row_stride(KBW), SS = KBW * 64;
+  uint8_t* sA = lds + wave * dw_bytes(Mmax, KBW);
+  uint8_t* sS = sA + dw_rows_bytes(Mmax, KBW);
 
-  u32x2 bcg = {0u, 0u}, bcu = {0u, 0u};
-  if (q == 0) {
-    bcg[0] = bf16_pair(cg, cg);
-    bcg[1] = f32_to_bf16(cg);
-    bcu[0] = bf16_pair(cu, cu);
-    bcu[1] = f32_to_bf16(cu);
+  // 1. this wave's slice of the rows and sums -> its LDS region.  A lane
+  //    whose bytes fall in a row's padding, past the slice or past the last
+  //    row copies the first bytes of row 0 (never read back).
+  {
+    const int n_a = dw_rows_bytes(M, KBW) / 1024;
+    for (int i = 0; i < n_a; ++i) {
+      const int off = i * 1024 + lane * 16;
+      int c = off / RS;
+      const int within = off % RS;
+      const bool ok = c < M && within < nkb * 256;
+      c = ok ? c : 0;
+      int src = src_row[0];
+#pragma unroll
+      for (int cc = 1; cc < kDecMaxRows; ++cc) src = c == cc ? src_row[cc] : src;
+      const uint8_t* g = reinterpret_cast<const uint8_t*>(A + (size_t)src * K) +
+                         (ok ? kb0 * 256 + within : 0);
+      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(sA + i * 1024), 16, 0, 0);
+    }
+    const int n_s = dw_sum_bytes(M, KBW) / 1024;
+    for (int i = 0; i < n_s; ++i) {
+      const int off = i * 1024 + lane * 16;
+      int c = off / SS;
+      const int within = off % SS;
+      const bool ok = c < M && within < nkb * 64;
+      c = ok ? c : 0;
+      int src = src_row[0];
+#pragma unroll
+      for (int cc = 1; cc < kDecMaxRows; ++cc) src = c == cc ? src_row[cc] : src;
+      const uint8_t* g = Asum + (size_t)src * G * 16 + (ok ? kb0 * 64 + within : 0);
+      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(sS + i * 1024), 16, 0, 0);
+    }
   }
-  f32x4 ag[2], au[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nt0 = grp * 2;
-  const uint8_t* g0 = blob + pg.off;
-  const uint8_t* u0 = blob + pu.off;
+  __builtin_amdgcn_sched_barrier(0);
 
-  for (int kbase = kb0; kbase < kb1; kbase += MAXKB) {
-    u32x2 wg[MAXKB][2], wu[MAXKB][2], sg[MAXKB][2], su[MAXKB][2];
-    uint32_t hg[MAXKB][2], hu[MAXKB][2];
-    u32x4 ax[MAXKB][4];
-    u32x2 ac[MAXKB][4];
+  // 2. packed tiles of this wave's k-blocks: codes (8 B / lane), level bit 2
+  //    (4 B / lane, 3-bit only), scales of row r, groups q & 2 and (q & 2) + 1
+  //    (4 B / lane).  The
+  //    loads are unconditional (a wave past the last k-block re-reads the last
+  //    tile) so that their number is a compile-time constant.
+  const int nt0 = GATEUP ? grp : grp * 4;
+  u32x2 wc[KBW][NS];
+  uint32_t wh[KBW][NS], ws[KBW][NS];
 #pragma unroll
-    for (int i = 0; i < MAXKB; ++i) {
-      const int kb = kbase + i;
-      if (kb < kb1) {
+  for (int i = 0; i < KBW; ++i) {
+    const int kbc = min(kb0 + i, KB - 1);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const size_t tile = (size_t)(nt0 + nt) * KB + kb;
-          wg[i][nt] = *reinterpret_cast<const u32x2*>(g0 + tile * 512 + lane * 8);
-          wu[i][nt] = *reinterpret_cast<const u32x2*>(u0 + tile * 512 + lane * 8);
-          if constexpr (QG3) hg[i][nt] = *reinterpret_cast<const uint32_t*>(g0 + pg.plane1 + tile * 256 + lane * 4);
-          else hg[i][nt] = 0;
-          if constexpr (QU3) hu[i][nt] = *reinterpret_cast<const uint32_t*>(u0 + pu.plane1 + tile * 256 + lane * 4);
-          else hu[i][nt] = 0;
-          sg[i][nt] = *reinterpret_cast<const u32x2*>(g0 + pg.scales + tile * 128 + r * 8);
-          su[i][nt] = *reinterpret_cast<const u32x2*>(u0 + pu.scales + tile * 128 + r * 8);
-        }
+    for (int j = 0; j < NS; ++j) {
+      const int second = GATEUP && j == 1;
+      const bool q3 = second ? QB3 : QA3;
+      const uint8_t* base = code_base[second];
+      const size_t tile = (size_t)(GATEUP ? nt0 : nt0 + j) * KB + kbc;
+      wc[i][j] = *reinterpret_cast<const u32x2*>(base + tile * 512 + lane * 8);
+      wh[i][j] = q3 ? *reinterpret_cast<const uint32_t*>(base + plane1[second] + tile * 256 +
+                                                         lane * 4)
+                    : 0u;
+      ws[i][j] = *reinterpret_cast<const uint32_t*>(base + scale_off[second] + tile * 128 +
+                                                    (r * 4 + (q & 2)) * 2);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. vector-memory loads complete in issue order: with only the tile loads
+  //    outstanding, this wave's copies into LDS have landed.
+  constexpr int kTileLoads = KBW * ((2 + (QA3 ? 1 : 0)) + (NS - 1) * (2 + (QB3 ? 1 : 0)));
+  static_assert(kTileLoads <= 63, "vmcnt holds at most 63 outstanding loads");
+  // s_waitcnt vmcnt(kTileLoads), expcnt and lgkmcnt at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((kTileLoads & 15) | ((kTileLoads >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (!GATEUP) {
+    // (Wa, Sa, Wb, Sb) fp32 half sums -> staged sums of the 32-group, in place
+    for (int t = lane; t < M * KBW * 4; t += 64) {
+      const int m = t / (KBW * 4), g = t % (KBW * 4);
+      if (g < nkb * 4) {
+        uint8_t* p = sS + m * SS + g * 16;
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        *reinterpret_cast<uint4*>(p) = stage_sums(v.x + v.z, v.y + v.w);
+      }
+    }
+  }
+
+  // 4. matrix-core work
+  const u32x4 bca = corr_b_operand(q == 0, QA3, ca);
+  const u32x4 bcb = corr_b_operand(q == 0, QB3, cb);
+  const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1), lane_copy(uk.b2)};
+  const int arow = r < M ? r : 0;
+  const uint8_t* aptr = sA + arow * RS + q * 16;
+  const uint8_t* sptr = sS + arow * SS;
+  f32x4 acc[NS];
 #pragma unroll
-        for (int gb = 0; gb < 4; ++gb) {
-          if (tok_ok) {
-            ax[i][gb] = *reinterpret_cast<const u32x4*>(xrow + kb * 128 + gb * 32 + q * 8);
-            ac[i][gb] = (q == 0) ? *reinterpret_cast<const u32x2*>(srow + (kb * 4 + gb) * 4)
-                                 : u32x2{0u, 0u};
-          } else {
-            ax[i][gb] = u32x4{0u, 0u, 0u, 0u};
-            ac[i][gb] = u32x2{0u, 0u};
+  for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // MR accumulator rows per lane carry real rows: rows 4*(lane/16) + i, so
+  // with M == 1 only i = 0 does (and only in lanes 0..15)
+  auto work = [&](auto mr) {
+    constexpr int MR = decltype(mr)::value;
+#pragma unroll
+    for (int i = 0; i < KBW; ++i) {
+      if (i < nkb) {
+#pragma unroll
+        for (int GB = 0; GB < 4; ++GB) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(aptr + (i * 128 + GB * 32) * 2);
+          const u32x4 sv = *reinterpret_cast<const u32x4*>(sptr + (i * 4 + GB) * 16);
+          const f32x4 corr_a = mfma_corr(sv, bca);
+          f32x4 corr_b = corr_a;
+          if constexpr (!SAMEC) corr_b = mfma_corr(sv, bcb);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const bool second = GATEUP && j == 1;
+            const bool q3 = second ? QB3 : QA3;
+            const uint32_t word = (GB < 2) ? wc[i][j][0] : wc[i][j][1];
+            u32x4 b;
+            if (q3) {
+              if (GB == 0) b = unpack3<0>(word, wh[i][j]);
+              if (GB == 1) b = unpack3<1>(word, wh[i][j]);
+              if (GB == 2) b = unpack3<2>(word, wh[i][j]);
+              if (GB == 3) b = unpack3<3>(word, wh[i][j]);
+            } else {
+              b = (GB & 1) ? unpack2_r<1>(word, ur) : unpack2_r<0>(word, ur);
+            }
+            const f32x4 dd = mfma32(a, b, second ? corr_b : corr_a);
+            // lane GB*16 + r holds scales (r, GB & 2) and (r, (GB & 2) + 1)
+            const uint32_t sw = (uint32_t)__shfl((int)ws[i][j], GB * 16 + r, 64);
+            const float s = f16_to_f32((GB & 1) ? (sw >> 16) : sw);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) acc[j][m] = fmaf(s, dd[m], acc[j][m]);
           }
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < MAXKB; ++i) {
-      if (kbase + i < kb1) {
-#define BQ_GU_STEP(GB)                                                                \
-  {                                                                                   \
-    const f32x4 cgc = mfma_corr(ac[i][GB], bcg);                                      \
-    const f32x4 cuc = (QG3 == QU3 && cg == cu) ? cgc : mfma_corr(ac[i][GB], bcu);     \
-    group_step<QG3, GB>(ag[0], ax[i][GB], wg[i][0], hg[i][0], sg[i][0], cgc);          \
-    group_step<QG3, GB>(ag[1], ax[i][GB], wg[i][1], hg[i][1], sg[i][1], cgc);          \
-    group_step<QU3, GB>(au[0], ax[i][GB], wu[i][0], hu[i][0], su[i][0], cuc);          \
-    group_step<QU3, GB>(au[1], ax[i][GB], wu[i][1], hu[i][1], su[i][1], cuc);          \
-  }
-        BQ_GU_STEP(0)
-        BQ_GU_STEP(1)
-        BQ_GU_STEP(2)
-        BQ_GU_STEP(3)
-#undef BQ_GU_STEP
-      }
-    }
-  }
-  // cross-wave reduction in a fixed order
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    red[wave][0 + i][lane] = ag[0][i];
-    red[wave][4 + i][lane] = ag[1][i];
-    red[wave][8 + i][lane] = au[0][i];
-    red[wave][12 + i][lane] = au[1][i];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 2 * 4 * 64; idx += 64 * KSPLIT) {
-    const int nt = idx >> 8, i = (idx >> 6) & 3, ln = idx & 63;
-    const int t = 4 * (ln >> 4) + i;
-    const int nn = nt * 16 + (ln & 15);
-    float g = 0.f, u = 0.f;
-    for (int w = 0; w < KSPLIT; ++w) {
-      g += red[w][nt * 4 + i][ln];
-      u += red[w][8 + nt * 4 + i][ln];
-    }
-    if (t < M) {
-      const uint32_t hb = f32_to_bf16(silu_f(g) * u);
-      const float hf = bf16_to_f32(hb);
-      hs[(size_t)(row0 + t) * I + grp * 32 + nn] = (uint16_t)f32_to_bf16(hf * 0.0625f);
-      hval[t][nn] = hf;
-    }
-  }
-  __syncthreads();
-  // 32-group sums of h for the down projection's correction term
-  if (threadIdx.x < 16 * 32) {
-    const int t = threadIdx.x >> 5, j = threadIdx.x & 31;
-    float s = (t < M) ? hval[t][j] : 0.f;
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
-    if (t < M && j == 0)
-      *reinterpret_cast<uint2*>(hsum + ((size_t)(row0 + t) * (I / 32) + grp) * 4) = split3_neg(s);
-  }
-}
+  };
+  if (M == 1)
+    work(std::integral_constant<int, 1>{});
+  else
+    work(std::integral_constant<int, 4>{});
 
-// ------------------------------------------------------- down + combine
-// Block = (slot, 64 output columns = 4 n-tiles).  y is rounded to bf16 and
-// stored; the last block to finish a column range (arrival counter) adds the
-// weighted expert outputs of every token for that range in a fixed order.
-template <bool QD3, int KSPLIT, int MAXKB>
-__global__ __launch_bounds__(64 * KSPLIT) void k_dec_down(
-    const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
-    ProjDesc pd, const int32_t* __restrict__ slots, const uint16_t* __restrict__ hs,
-    const uint16_t* __restrict__ hsum, int d, int I, int T, int k, int n_shared, float cd,
-    uint16_t* __restrict__ y, uint32_t* __restrict__ counters, const int32_t* __restrict__ inv_row,
-    const float* __restrict__ topk_w, const uint16_t* __restrict__ x, int residual,
-    uint16_t* __restrict__ out) {
-  constexpr int NTW = 4;
-  __shared__ float red[KSPLIT][NTW * 4][64];
-  __shared__ int s_last;
-  const int blocks_per_slot = d / (16 * NTW);
-  const int slot = blockIdx.x / blocks_per_slot, cb = blockIdx.x % blocks_per_slot;
-  const int n_slots = slots[0];
-  if (slot >= n_slots) return;
-  const int e = slots[1 + 3 * slot], row0 = slots[2 + 3 * slot], M = slots[3 + 3 * slot];
-  const uint8_t* blob = (e >= 0 ? experts + (size_t)e * stride : shared) + pd.off;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
-  const int KB = I / 128;
-  const int per = (KB + KSPLIT - 1) / KSPLIT;
-  const int kb0 = min(KB, wave * per), kb1 = min(KB, kb0 + per);
-  const bool tok_ok = r < M;
-  const uint16_t* hrow = hs + (size_t)(row0 + (tok_ok ? r : 0)) * I;
-  const uint16_t* srow = hsum + (size_t)(row0 + (tok_ok ? r : 0)) * (I / 32) * 4;
-  u32x2 bc = {0u, 0u};
-  if (q == 0) {
-    bc[0] = bf16_pair(cd, cd);
-    bc[1] = f32_to_bf16(cd);
+  // 5. cross-wave reduction in a fixed order (every wave is done with LDS)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);  // [KSPLIT][NS][4][32 lanes]
+  if (lane < 32) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((wave * NS + j) * 4 + i) * 32 + lane] = acc[j][i];
   }
-  f32x4 acc[NTW];
-#pragma unroll
-  for (int j = 0; j < NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nt0 = cb * NTW;
-  for (int kbase = kb0; kbase < kb1; kbase += MAXKB) {
-    u32x2 wd[MAXKB][NTW], sd[MAXKB][NTW];
-    uint32_t hd[MAXKB][NTW];
-    u32x4 ax[MAXKB][4];
-    u32x2 ac[MAXKB][4];
-#pragma unroll
-    for (int i = 0; i < MAXKB; ++i) {
-      const int kb = kbase + i;
-      if (kb < kb1) {
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const size_t tile = (size_t)(nt0 + j) * KB + kb;
-          wd[i][j] = *reinterpret_cast<const u32x2*>(blob + tile * 512 + lane * 8);
-          if constexpr (QD3) hd[i][j] = *reinterpret_cast<const uint32_t*>(blob + pd.plane1 + tile * 256 + lane * 4);
-          else hd[i][j] = 0;
-          sd[i][j] = *reinterpret_cast<const u32x2*>(blob + pd.scales + tile * 128 + r * 8);
+  __syncthreads();
+  if constexpr (GATEUP) {
+    // 16 threads per row (whole 16-lane segments of waves 0 and 1)
+    if (tid < kDecMaxRows * 16) {
+      const int row = tid >> 4, col = tid & 15;
+      const int ln = 16 * (row >> 2) + col, i = row & 3;
+      float hf = 0.f;
+      if (row < M) {
+        float g = 0.f, u = 0.f;
+        for (int w = 0; w < KSPLIT; ++w) {
+          g += red[((w * 2 + 0) * 4 + i) * 32 + ln];
+          u += red[((w * 2 + 1) * 4 + i) * 32 + ln];
         }
-#pragma unroll
-        for (int gb = 0; gb < 4; ++gb) {
-          if (tok_ok) {
-            ax[i][gb] = *reinterpret_cast<const u32x4*>(hrow + kb * 128 + gb * 32 + q * 8);
-            ac[i][gb] = (q == 0) ? *reinterpret_cast<const u32x2*>(srow + (kb * 4 + gb) * 4)
-                                 : u32x2{0u, 0u};
-          } else {
-            ax[i][gb] = u32x4{0u, 0u, 0u, 0u};
-            ac[i][gb] = u32x2{0u, 0u};
-          }
-        }
+        hf = bf16_to_f32(f32_to_bf16(silu_f(g) * u));
+        out[(size_t)(row0 + row) * N + grp * 16 + col] = (uint16_t)f32_to_bf16(hf * 0.0625f);
       }
-    }
+      // (W, S) of h over this tile's 16 columns: k-slots 16*(grp%2) + col of
+      // the down projection's 32-group grp/2
+      float sw = hf * slot_weight(16 * (grp & 1) + col), s = hf;
 #pragma unroll
-    for (int i = 0; i < MAXKB; ++i) {
-      if (kbase + i < kb1) {
-#define BQ_DN_STEP(GB)                                                        \
-  {                                                                           \
-    const f32x4 cc = mfma_corr(ac[i][GB], bc);                                \
-    _Pragma("unroll") for (int j = 0; j < NTW; ++j)                           \
-        group_step<QD3, GB>(acc[j], ax[i][GB], wd[i][j], hd[i][j], sd[i][j], cc); \
-  }
-        BQ_DN_STEP(0)
-        BQ_DN_STEP(1)
-        BQ_DN_STEP(2)
-        BQ_DN_STEP(3)
-#undef BQ_DN_STEP
+      for (int o = 8; o > 0; o >>= 1) {
+        sw += __shfl_xor(sw, o, 16);
+        s += __shfl_xor(s, o, 16);
       }
+      if (row < M && col == 0)
+        *reinterpret_cast<float2*>(out_psum + ((size_t)(row0 + row) * (N / 16) + grp) * 2) =
+            make_float2(sw, s);
+    }
+  } else {
+    for (int t = tid; t < M * 64; t += 64 * KSPLIT) {
+      const int row = t >> 6, j = (t >> 4) & 3, col = t & 15;
+      const int ln = 16 * (row >> 2) + col, i = row & 3;
+      float s = 0.f;
+      for (int w = 0; w < KSPLIT; ++w) s += red[((w * 4 + j) * 4 + i) * 32 + ln];
+      out[(size_t)(row0 + row) * N + (nt0 + j) * 16 + col] = (uint16_t)f32_to_bf16(s);
     }
   }
-#pragma unroll
-  for (int j = 0; j < NTW; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][j * 4 + i][lane] = acc[j][i];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < NTW * 4 * 64; idx += 64 * KSPLIT) {
-    const int j = idx >> 8, i = (idx >> 6) & 3, ln = idx & 63;
-    const int t = 4 * (ln >> 4) + i;
-    float s = 0.f;
-    for (int w = 0; w < KSPLIT; ++w) s += red[w][j * 4 + i][ln];
-    if (t < M) y[(size_t)(row0 + t) * d + (nt0 + j) * 16 + (ln & 15)] = (uint16_t)f32_to_bf16(s);
-  }
-  // arrival: the last block of this column range combines
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(&counters[cb], 1u);
-    s_last = (old == (uint32_t)(n_slots - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int cols = 16 * NTW;
-  for (int idx = threadIdx.x; idx < T * cols; idx += 64 * KSPLIT) {
-    const int t = idx / cols, c = cb * cols + idx % cols;
-    float a = residual ? bf16_to_f32(x[(size_t)t * d + c]) : 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int rr = inv_row[(size_t)t * k + j];
-      a = fmaf(topk_w[(size_t)t * k + j], bf16_to_f32(__builtin_nontemporal_load(y + (size_t)rr * d + c)), a);
-    }
-    if (n_shared) a += bf16_to_f32(__builtin_nontemporal_load(y + (size_t)(T * k + t) * d + c));
-    out[(size_t)t * d + c] = (uint16_t)f32_to_bf16(a);
-  }
-  if (threadIdx.x == 0) counters[cb] = 0u;
 }
 
 int launch_decode_route(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
-                        moe_routing* R, uint8_t* ws, const DecodeWs& W, void* stream);
+                        moe_routing* R, uint8_t* ws, const DecodeWs& W, void* stream,
+                        uint32_t mask);
 
 static ProjDesc proj(const moe_layer* L, int m) {
   const int q = m == 0 ? L->q_gate : m == 1 ? L->q_up : L->q_down;
@@ -332,53 +329,126 @@ static ProjDesc proj(const moe_layer* L, int m) {
   return p;
 }
 
-template <bool QG3, bool QU3>
-static void launch_gateup(const moe_layer* L, dim3 grid, hipStream_t s, ProjDesc pg, ProjDesc pu,
-                          const int32_t* slots, const int32_t* perm_tok, const uint16_t* xs,
-                          const uint16_t* xsum, int Tk, uint16_t* hs, uint16_t* hsum) {
-  hipLaunchKernelGGL((k_dec_gateup<QG3, QU3, 8, 4>), grid, dim3(512), 0, s,
-                     (const uint8_t*)L->experts, L->expert_stride, (const uint8_t*)L->shared, pg,
-                     pu, slots, perm_tok, xs, xsum, L->d, L->inter, Tk, corr_const(L->q_gate),
-                     corr_const(L->q_up), hs, hsum);
+// Launch shape of one projection: waves per block (split of the reduction
+// dimension) and k-blocks per wave, each wave owning at most 16
+// (stream, k-block) tiles.
+struct DecShape {
+  int ksplit, kbw;
+};
+
+static DecShape dec_shape(bool gateup, int K) {
+  const int KB = K / 128, cap = gateup ? 8 : 4;
+  int ks = 4;
+  while (ks < (gateup ? 8 : 16) && (KB + ks - 1) / ks > cap) ks *= 2;
+  const int per = (KB + ks - 1) / ks;
+  if (per > cap) return {0, 0};
+  int kbw = 2;
+  while (kbw < per) kbw *= 2;
+  return {ks, kbw};
+}
+
+static size_t dec_lds_bytes(bool gateup, DecShape sh, int Mmax) {
+  const size_t rows = (size_t)sh.ksplit * dw_bytes(Mmax, sh.kbw);
+  const size_t red = (size_t)sh.ksplit * (gateup ? 2 : 4) * 4 * 32 * 4;
+  return rows > red ? rows : red;
+}
+
+constexpr size_t kLdsLimit = 160 * 1024;
+
+bool decode_shape_ok(const moe_layer* L, int T) {
+  const int Mmax = T < kDecMaxRows ? T : kDecMaxRows;
+  const DecShape gu = dec_shape(true, L->d), dn = dec_shape(false, L->inter);
+  return gu.ksplit && dn.ksplit && dec_lds_bytes(true, gu, Mmax) <= kLdsLimit &&
+         dec_lds_bytes(false, dn, Mmax) <= kLdsLimit;
+}
+
+template <bool GATEUP, bool QA3, bool QB3, bool SAMEC>
+static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const moe_layer* L,
+                       ProjDesc pa, ProjDesc pb, const int32_t* slots, const uint16_t* A,
+                       const uint8_t* Asum, int K, int N, float ca, float cb, uint16_t* out,
+                       float* psum) {
+  const size_t lds = dec_lds_bytes(GATEUP, sh, Mmax);
+#define BQ_L(KS, KBW)                                                                       \
+  hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW>), dim3(n_blocks),        \
+                     dim3(64 * KS), lds, s, (const uint8_t*)L->experts, L->expert_stride,   \
+                     (const uint8_t*)L->shared, pa, pb, slots, A, Asum, K, N, Mmax, ca, cb, \
+                     out, psum, kUnpack2)
+  if (sh.ksplit == 4 && sh.kbw == 2)
+    BQ_L(4, 2);
+  else if (sh.ksplit == 4 && sh.kbw == 4)
+    BQ_L(4, 4);
+  else if constexpr (GATEUP) {
+    if (sh.ksplit == 4 && sh.kbw == 8)
+      BQ_L(4, 8);
+    else if (sh.ksplit == 8 && sh.kbw == 8)
+      BQ_L(8, 8);
+    else
+      return -1;
+  } else {
+    if (sh.ksplit == 8 && sh.kbw == 4)
+      BQ_L(8, 4);
+    else if (sh.ksplit == 16 && sh.kbw == 4)
+      BQ_L(16, 4);
+    else
+      return -1;
+  }
+#undef BQ_L
+  return 0;
 }
 
 int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
-                  uint8_t* ws, const DecodeWs& W, uint16_t* out, void* stream) {
-  int rc = launch_decode_route(L, x, T, flags, R, ws, W, stream);
+                  uint8_t* ws, const DecodeWs& W, uint16_t* out, void* stream, uint32_t mask) {
+  int rc = launch_decode_route(L, x, T, flags, R, ws, W, stream, mask);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const int k = L->top_k, d = L->d, I = L->inter;
-  const int Tk = T * k;
-  const ProjDesc pg = proj(L, 0), pu = proj(L, 1), pdn = proj(L, 2);
+  const int Mmax = T < kDecMaxRows ? T : kDecMaxRows;
   const int32_t* slots = (const int32_t*)(ws + W.slots);
-  uint16_t* xs = (uint16_t*)(ws + W.xs);
-  uint16_t* xsum = (uint16_t*)(ws + W.xsum);
+  const uint16_t* xs = (const uint16_t*)(ws + W.xs);
+  const uint8_t* xsum = ws + W.xsum;
   uint16_t* hs = (uint16_t*)(ws + W.hs);
-  uint16_t* hsum = (uint16_t*)(ws + W.hsum);
-  dim3 g1(W.max_slots * (I / 32));
-  const bool g3 = L->q_gate == MOE_Q_INT3, u3 = L->q_up == MOE_Q_INT3;
-  if (g3 && u3)
-    launch_gateup<true, true>(L, g1, s, pg, pu, slots, R->perm_tok, xs, xsum, Tk, hs, hsum);
-  else if (g3)
-    launch_gateup<true, false>(L, g1, s, pg, pu, slots, R->perm_tok, xs, xsum, Tk, hs, hsum);
-  else if (u3)
-    launch_gateup<false, true>(L, g1, s, pg, pu, slots, R->perm_tok, xs, xsum, Tk, hs, hsum);
-  else
-    launch_gateup<false, false>(L, g1, s, pg, pu, slots, R->perm_tok, xs, xsum, Tk, hs, hsum);
-  dim3 g2(W.max_slots * (d / 64));
-  const int residual = (flags & MOE_ADD_RESIDUAL) ? 1 : 0;
+  float* hsum = (float*)(ws + W.hsum);
   uint16_t* y = (uint16_t*)(ws + W.y);
-  uint32_t* counters = (uint32_t*)(ws + W.counters);
-  if (L->q_down == MOE_Q_INT3)
-    hipLaunchKernelGGL((k_dec_down<true, 8, 2>), g2, dim3(512), 0, s, (const uint8_t*)L->experts,
-                       L->expert_stride, (const uint8_t*)L->shared, pdn, slots, hs, hsum, d, I, T,
-                       k, L->n_shared, corr_const(L->q_down), y, counters, R->inv_row, R->topk_w,
-                       x, residual, out);
-  else
-    hipLaunchKernelGGL((k_dec_down<false, 8, 2>), g2, dim3(512), 0, s, (const uint8_t*)L->experts,
-                       L->expert_stride, (const uint8_t*)L->shared, pdn, slots, hs, hsum, d, I, T,
-                       k, L->n_shared, corr_const(L->q_down), y, counters, R->inv_row, R->topk_w,
-                       x, residual, out);
+  if (mask & MOE_DECODE_STAGE_GATEUP) {
+    const ProjDesc pg = proj(L, 0), pu = proj(L, 1);
+    const DecShape sh = dec_shape(true, d);
+    const int nb = W.max_slots * (I / 16);
+    const float cg = qtype_offset(L->q_gate), cu = qtype_offset(L->q_up);
+    const bool g3 = L->q_gate == MOE_Q_INT3, u3 = L->q_up == MOE_Q_INT3;
+    const bool same = L->q_gate == L->q_up;
+#define BQ_GU(A3, B3, SC)                                                                   \
+  rc = launch_proj<true, A3, B3, SC>(sh, nb, Mmax, s, L, pg, pu, slots, xs, xsum, d, I, cg, \
+                                     cu, hs, hsum)
+    if (g3 && u3)
+      BQ_GU(true, true, true);
+    else if (g3)
+      BQ_GU(true, false, false);
+    else if (u3)
+      BQ_GU(false, true, false);
+    else if (same)
+      BQ_GU(false, false, true);
+    else
+      BQ_GU(false, false, false);
+#undef BQ_GU
+    if (rc) return rc;
+  }
+  if (mask & MOE_DECODE_STAGE_DOWN) {
+    const ProjDesc pd = proj(L, 2);
+    const DecShape sh = dec_shape(false, I);
+    const int nb = W.max_slots * (d / 64);
+    const float cd = qtype_offset(L->q_down);
+    const uint8_t* hsb = (const uint8_t*)hsum;
+    if (L->q_down == MOE_Q_INT3)
+      rc = launch_proj<false, true, true, true>(sh, nb, Mmax, s, L, pd, pd, slots, hs, hsb, I, d,
+                                                cd, cd, y, nullptr);
+    else
+      rc = launch_proj<false, false, false, true>(sh, nb, Mmax, s, L, pd, pd, slots, hs, hsb, I,
+                                                  d, cd, cd, y, nullptr);
+    if (rc) return rc;
+    rc = launch_combine(y, T, d, k, L->n_shared, R->inv_row, R->topk_w, x,
+                        (flags & MOE_ADD_RESIDUAL) ? 1 : 0, out, stream);
+    if (rc) return rc;
+  }
   return (int)hipGetLastError();
 }
 

@@ -39,22 +39,73 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-// Correction term of one 32-group as a 16x16x32 op (same shape as the main op,
-// so the main op can take it as its C operand without a mixed-shape dependency):
-// lanes 0..15 put the row's bf16 triple (-hi, -mid, -lo, 0) in k-slots 0..3 of A
-// and (c, c, c, 0) in k-slots 0..3 of B; every other slot is zero.  Result:
-// D[row][col] = -c * (hi + mid + lo)[row] for every column.
-__device__ __forceinline__ f32x4 mfma_corr(u32x2 a, u32x2 b) {
-  const u32x4 a4 = {a[0], a[1], 0u, 0u}, b4 = {b[0], b[1], 0u, 0u};
-  return mfma32(a4, b4, f32x4{0.f, 0.f, 0.f, 0.f});
+// Correction term of one 32-group as a zero-padded 16x16x32 op (the same
+// shape as the main op, which takes it as its C operand).  Lanes 0..15 hold
+// their row's staged sums in k-slots 0..7 of A: (-W, -S) as two negated bf16
+// triples and two zeros, where S = sum_k x_k and W = sum_k x_k * base_k / 16
+// (see unpack2); lanes 0..15 hold the per-format constants in k-slots 0..7 of
+// B, zeros elsewhere.  D[row][col] = -(b0 * W + b3 * S)[row] for every column.
+__device__ __forceinline__ f32x4 mfma_corr(u32x4 a, u32x4 b) {
+  return mfma32(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+}
+
+// bf16 bits of x split into hi + mid + lo (each an exact bf16; the sum is x to
+// ~2^-24 relative), negated.
+__device__ __forceinline__ void split3_neg(float s, uint32_t& a, uint32_t& b, uint32_t& c) {
+  const uint32_t hi = f32_to_bf16(s);
+  const float r1 = s - bf16_to_f32(hi);
+  const uint32_t mid = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(mid);
+  const uint32_t lo = f32_to_bf16(r2);
+  a = hi ^ 0x8000u;
+  b = mid ^ 0x8000u;
+  c = lo ^ 0x8000u;
+}
+
+// Staged sums of one (row, 32-group): 8 bf16 = (-W, -S) triples + 2 zeros.
+__device__ __forceinline__ uint4 stage_sums(float W, float S) {
+  uint32_t w0, w1, w2, s0, s1, s2;
+  split3_neg(W, w0, w1, w2);
+  split3_neg(S, s0, s1, s2);
+  uint4 v;
+  v.x = (w0 & 0xFFFFu) | (w1 << 16);
+  v.y = (w2 & 0xFFFFu) | (s0 << 16);
+  v.z = (s1 & 0xFFFFu) | (s2 << 16);
+  v.w = 0u;
+  return v;
+}
+
+// The B operand of the correction op for a projection: 2-bit formats subtract
+// W + offset * S, 3-bit formats (all slots at base 128) subtract (8 + offset) * S.
+__device__ __forceinline__ u32x4 corr_b_operand(bool lane_active, bool q3, float off) {
+  u32x4 b = {0u, 0u, 0u, 0u};
+  if (lane_active) {
+    const uint32_t one = 0x3F80u;
+    const uint32_t c = f32_to_bf16(q3 ? 8.0f + off : off);
+    const uint32_t w = q3 ? 0u : one;
+    b[0] = w | (w << 16);
+    b[1] = w | (c << 16);
+    b[2] = c | (c << 16);
+  }
+  return b;
+}
+
+// Weight base_k / 16 of k-slot j (position inside its 32-group) in W.
+__device__ __forceinline__ float slot_weight(int j) {
+  const int v = (j & 7) >> 1;
+  return v == 0 ? 128.0f : v == 1 ? 32.0f : 8.0f;
 }
 
 // ---------------------------------------------------------- code unpacking
 // A lane's 32-bit plane-0 word holds two groups (parity 0 / 1) x 8 k-slots.
 // k-slot s = 2v + h of group parity p sits at bit 16h + 2(4p + v).  The
-// matrix-core operand wants slots (2v, 2v+1) in the low/high half of VGPR v,
-// each as the bf16 value 128 + 16u: move the field to bits [5:4] of each half
-// and or in 0x4300 (= 128.0).
+// matrix-core operand wants slots (2v, 2v+1) in the low/high half of VGPR v.
+// 2-bit levels become bf16 values base_v + 16u: the fields of v = 0, 1, 2 stay
+// where they are (bits [1:0], [3:2], [5:4] of each half, after a shift by 8
+// for parity 1) under the bases 2048 (0x4500), 512 (0x4400) and 128 (0x4300),
+// whose unit in the last place is 16, 4 and 1; v = 3 is shifted down to bits
+// [5:4] under base 128.  So one mask-and-or per pair of levels, plus two
+// shifts per 8 levels.
 template <int S>
 __device__ __forceinline__ uint32_t shl_signed(uint32_t w) {
   if constexpr (S >= 0)
@@ -75,11 +126,12 @@ __device__ __forceinline__ uint32_t hi_field(uint32_t w1) {
 
 template <int P>
 __device__ __forceinline__ u32x4 unpack2(uint32_t w) {
+  const uint32_t x = P ? (w >> 8) : w;
   u32x4 r;
-  r[0] = lo_field<4 * P + 0>(w) | 0x43004300u;
-  r[1] = lo_field<4 * P + 1>(w) | 0x43004300u;
-  r[2] = lo_field<4 * P + 2>(w) | 0x43004300u;
-  r[3] = lo_field<4 * P + 3>(w) | 0x43004300u;
+  r[0] = (x & 0x00030003u) | 0x45004500u;
+  r[1] = (x & 0x000C000Cu) | 0x44004400u;
+  r[2] = (x & 0x00300030u) | 0x43004300u;
+  r[3] = ((x >> 2) & 0x00300030u) | 0x43004300u;
   return r;
 }
 

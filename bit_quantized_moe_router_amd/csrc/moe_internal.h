@@ -31,23 +31,27 @@ struct ProjDesc {
   int32_t K, N;
 };
 
-// Magic-number operand encoding used by the kernels: a level u becomes the
-// bf16 value 128 + 16u (exact), activations are pre-scaled by 1/16 (exact),
-// so each product is x*(8 + u); the per-group term (8 + offset) * sum(x) is
-// removed through a second matrix-core op.  corr_const(q) = 8 + offset.
-inline float corr_const(int q) { return 8.0f + qtype_offset(q); }
-
+// Operand encoding used by the kernels: a level u becomes an exact bf16 value
+// base + 16u (base 2048, 512 or 128 by k-slot, see unpack2 / unpack3),
+// activations are pre-scaled by 1/16, and the per-group term
+// sum_k x_k * (base_k / 16 + offset) is removed by a second matrix-core op on
+// staged sums (W = sum x_k * base_k / 16, S = sum x_k).
+// Decode slot list: a 16-int header (n_slots first), then one 16-int record per
+// slot: expert (-1 = shared), first permuted row, row count M, unused, and the
+// token of each of the M rows.
+constexpr int kSlotRec = 16;
+constexpr int kSlotTok = 4;
 constexpr int kDecodeMaxRoutedRows = 64;  // T*k for the decode path
 constexpr int kDecodeMaxRows = 72;        // T*(k + n_shared) for the decode path
+constexpr int kDecodeMaxDim = 8192;       // d and inter for the decode path
 
 // Workspace layouts (byte offsets from the workspace base).
 struct DecodeWs {
   size_t slots;     // int32 [1 + 3*max_slots]: n_slots, then (expert|-1, row0, rows)
-  size_t counters;  // uint32 [d/64] combine arrival counters
   size_t xs;        // bf16 [T][d]        x / 16
-  size_t xsum;      // bf16 [T][d/32][4]  -(hi, mid, lo) of each 32-group sum of x, 0
+  size_t xsum;      // bf16 [T][d/32][8]  staged sums (W, S) of each 32-group of x
   size_t hs;        // bf16 [rows][I]     h / 16
-  size_t hsum;      // bf16 [rows][I/32][4]
+  size_t hsum;      // fp32 [rows][I/16][2] (W, S) sums of h over each 16 columns
   size_t y;         // bf16 [rows][d]
   size_t total;
   int max_slots, rows;
@@ -59,9 +63,9 @@ struct PrefillWs {
   size_t tiles;     // int32 [max_tiles][4] (expert|-1, row0, rows, 0) + int32 count (at ctrl)
   size_t ctrl;      // int32 [16] counters
   size_t xs;        // bf16 [T][d]        x / 16
-  size_t xsum;      // bf16 [T][d/32][4]  negated bf16 triple of each 32-group sum of x
+  size_t xsum;      // bf16 [T][d/32][8]  staged sums (W, S) of each 32-group of x
   size_t h;         // bf16 [rows][I]     h / 16
-  size_t hsum;      // bf16 [rows][I/32][4]
+  size_t hsum;      // bf16 [rows][I/32][8] staged sums of h
   size_t y;         // bf16 [rows][d]
   size_t total;
   int nblk, max_tiles, rows;
@@ -77,9 +81,16 @@ PrefillWs prefill_ws_layout(const moe_layer* L, int T);
 // All return hipSuccess (0) or the launch error code.
 int launch_route_generic(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
                          moe_routing* R, uint8_t* ws, const PrefillWs& P, void* stream);
+// `mask` selects the kernels to enqueue (bit i = stage i, see moe.h); ~0u runs all.
+// Whether the decode kernels take this layer for T tokens (LDS and register
+// limits of their launch shapes).
+bool decode_shape_ok(const moe_layer* L, int T);
 int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
-                  uint8_t* ws, const DecodeWs& W, uint16_t* out, void* stream);
+                  uint8_t* ws, const DecodeWs& W, uint16_t* out, void* stream, uint32_t mask);
 int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
-                   uint8_t* ws, const PrefillWs& P, uint16_t* out, void* stream);
+                   uint8_t* ws, const PrefillWs& P, uint16_t* out, void* stream, uint32_t mask);
+// out[t] = bf16([x[t]] + sum_j w[t][j] * y[inv_row[t][j]] + [y[T*k + t]]) for all T tokens
+int launch_combine(const uint16_t* y, int T, int d, int k, int n_shared, const int32_t* inv_row,
+                   const float* w, const uint16_t* x, int residual, uint16_t* out, void* stream);
 
 }  // namespace bqmoe

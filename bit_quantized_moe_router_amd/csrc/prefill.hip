@@ -27,19 +27,7 @@ constexpr int RT = kRows / 16;        // 16-row tiles per wave
 
 __device__ __forceinline__ float silu_pf(float g) { return g / (1.0f + expf(-g)); }
 
-__device__ __forceinline__ uint2 split3_neg_pf(float s) {
-  const uint32_t hi = f32_to_bf16(s);
-  const float r1 = s - bf16_to_f32(hi);
-  const uint32_t mid = f32_to_bf16(r1);
-  const float r2 = r1 - bf16_to_f32(mid);
-  const uint32_t lo = f32_to_bf16(r2);
-  uint2 v;
-  v.x = ((hi ^ 0x8000u) & 0xFFFFu) | (((mid ^ 0x8000u) & 0xFFFFu) << 16);
-  v.y = (lo ^ 0x8000u) & 0xFFFFu;
-  return v;
-}
-
-// Activation staging for prefill: xs = x/16 and negated bf16-triple 32-group sums.
+// Activation staging for prefill: xs = x/16 and the 32-group sums (W, S).
 __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ x, int T, int d,
                                                uint16_t* __restrict__ xs,
                                                uint16_t* __restrict__ xsum) {
@@ -51,10 +39,13 @@ __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ x, i
     const int g = (int)(p % G);
     const float xf = bf16_to_f32(x[t * d + g * 32 + j]);
     xs[t * d + g * 32 + j] = (uint16_t)f32_to_bf16(xf * 0.0625f);
-    float s = xf;
+    float sw = xf * slot_weight(j), s = xf;
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
-    if (j == 0) *reinterpret_cast<uint2*>(xsum + (t * G + g) * 4) = split3_neg_pf(s);
+    for (int o = 16; o > 0; o >>= 1) {
+      sw += __shfl_xor(sw, o, 32);
+      s += __shfl_xor(s, o, 32);
+    }
+    if (j == 0) *reinterpret_cast<uint4*>(xsum + (t * G + g) * 8) = stage_sums(sw, s);
   }
 }
 
@@ -74,14 +65,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // LDS per buffer: 16 chunk columns x kRows rows x 16 B of activations (chunk c
 // of row R at c*kRows*16 + R*16: the 16 rows a matrix-core read touches are 256
 // contiguous bytes, and every address is one base register plus an immediate),
-// then kRows rows x 32 B of group sums.  Both are filled with direct
-// global->LDS loads (64 lanes x 16 B = 64 rows of one chunk column per
-// instruction), which need no registers.
+// then kRows rows x 64 B of group sums (4 groups x 16 B).  Both are filled
+// with direct global->LDS loads (64 lanes x 16 B = 64 rows of one chunk column
+// per instruction), which need no registers.
 constexpr int kColBytes = kRows * 16;
-constexpr int kBufBytes = kRows * 256 + kRows * 32;
+constexpr int kBufBytes = kRows * 256 + kRows * 64;
 constexpr int kDmaA = 16 * kRows / 64;   // activation DMA instructions per k-block
-constexpr int kDmaS = kRows * 32 / 1024; // group-sum DMA instructions per k-block
-static_assert(kRows % 64 == 0 && kDmaA % 4 == 0, "tile rows");
+constexpr int kDmaS = kRows * 64 / 1024; // group-sum DMA instructions per k-block
+static_assert(kRows % 64 == 0 && kDmaA % 4 == 0 && kDmaS <= 4, "tile rows");
 
 template <int NMAT, int NTPW, bool Q3A, bool Q3B, bool SAMEC>
 __global__ __launch_bounds__(256, 2) void k_pf_gemm(
@@ -113,21 +104,17 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
   const uint16_t* arow[kRows / 64];
 #pragma unroll
   for (int h = 0; h < kRows / 64; ++h) arow[h] = A + (size_t)sTok[64 * h + lane] * K;
-  const int s_wave_row = (wave < kDmaS ? wave : 0) * 32 + (lane >> 1);
-  const uint16_t* srow = Asum + ((size_t)sTok[s_wave_row] * G + (lane & 1) * 2) * 4;
+  // group sums: instruction i covers rows 16*i .. 16*i+15, 4 lanes (groups) per row
+  const int s_wave_row = (wave < kDmaS ? wave : 0) * 16 + (lane >> 2);
+  const uint16_t* srow = Asum + ((size_t)sTok[s_wave_row] * G + (lane & 3)) * 8;
 
   // this wave's streams: stream j -> projection (j / NTPW), n-tile nt0 + j % NTPW
   const int nt0 = (blockIdx.y * 4 + wave) * NTPW;
   const uint8_t* const base0 = blob + pa.off;
   const uint8_t* const base1 = blob + pb.off;
 
-  u32x2 bc0 = {0u, 0u}, bc1 = {0u, 0u};
-  if (q == 0) {
-    bc0[0] = f32_to_bf16(ca) | (f32_to_bf16(ca) << 16);
-    bc0[1] = f32_to_bf16(ca);
-    bc1[0] = f32_to_bf16(cb) | (f32_to_bf16(cb) << 16);
-    bc1[1] = f32_to_bf16(cb);
-  }
+  const u32x4 bc0 = corr_b_operand(q == 0, Q3A, ca);
+  const u32x4 bc1 = corr_b_operand(q == 0, Q3B, cb);
 
   f32x4 acc[RT][4];
 #pragma unroll
@@ -150,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
                                        16, 0, 0);                                              \
     }                                                                                          \
     if (wave < kDmaS)                                                                          \
-      __builtin_amdgcn_global_load_lds((const void*)(srow + (KB_) * 16),                       \
+      __builtin_amdgcn_global_load_lds((const void*)(srow + (KB_) * 32),                       \
                                        (lds_void*)(dst + kRows * 256 + wave * 1024), 16, 0, 0); \
   }
 
@@ -193,8 +180,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
       sc[j] = f16_to_f32(sbits & 0xFFFFu);                                                      \
     }                                                                                           \
     _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                         \
-      const uint2 sv = *reinterpret_cast<const uint2*>(sS + (rt * 16 + r) * 32 + GB * 8);      \
-      const u32x2 av = {q == 0 ? sv.x : 0u, q == 0 ? sv.y : 0u};                                \
+      const uint4 sv = *reinterpret_cast<const uint4*>(sS + (rt * 16 + r) * 64 + GB * 16);     \
+      const u32x4 av = {q == 0 ? sv.x : 0u, q == 0 ? sv.y : 0u, q == 0 ? sv.z : 0u, 0u};         \
       const f32x4 corr0 = mfma_corr(av, bc0);                           \
       f32x4 corr1 = corr0;                                                                      \
       if constexpr (!SAMEC) corr1 = mfma_corr(av, bc1);               \
@@ -232,23 +219,28 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = rt * 16 + 4 * q + i;
-        float hsum_part = 0.f;
+        float hs_part = 0.f, hw_part = 0.f;
+        const float wgt = slot_weight(r);  // column nt*16 + r is k-slot (16 jn + r) of its group
 #pragma unroll
         for (int jn = 0; jn < NTPW; ++jn) {
           const float g = acc[rt][jn][i], u = acc[rt][NTPW + jn][i];
           const uint32_t hb = f32_to_bf16(silu_pf(g) * u);
           const float hf = bf16_to_f32(hb);
-          hsum_part += hf;
+          hs_part += hf;
+          hw_part += hf * wgt;
           if (m < M)
             out[(size_t)(row0 + m) * I + (nt0 + jn) * 16 + r] = (uint16_t)f32_to_bf16(hf * 0.0625f);
         }
         // sum over the 16 lanes holding this row (r = 0..15)
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) hsum_part += __shfl_xor(hsum_part, o, 16);
+        for (int o = 8; o > 0; o >>= 1) {
+          hs_part += __shfl_xor(hs_part, o, 16);
+          hw_part += __shfl_xor(hw_part, o, 16);
+        }
         if (m < M && r == 0) {
           const int g32 = (nt0 * 16) / 32;
-          *reinterpret_cast<uint2*>(out_sum + ((size_t)(row0 + m) * (I / 32) + g32) * 4) =
-              split3_neg_pf(hsum_part);
+          *reinterpret_cast<uint4*>(out_sum + ((size_t)(row0 + m) * (I / 32) + g32) * 8) =
+              stage_sums(hw_part, hs_part);
         }
       }
     }
@@ -341,14 +333,16 @@ static void launch_gu(dim3 grid, hipStream_t s, const moe_layer* L, ProjDesc pg,
                       const uint16_t* xs, const uint16_t* xsum, uint16_t* hs, uint16_t* hsum) {
   hipLaunchKernelGGL((k_pf_gemm<2, 2, A3, B3, SAMEC>), grid, dim3(256), 0, s, (const uint8_t*)L->experts,
                      L->expert_stride, (const uint8_t*)L->shared, pg, pu, tiles, ctrl, perm_tok, Tk,
-                     1, xs, xsum, L->d, L->inter, corr_const(L->q_gate), corr_const(L->q_up), hs,
+                     1, xs, xsum, L->d, L->inter, qtype_offset(L->q_gate), qtype_offset(L->q_up), hs,
                      hsum);
 }
 
 int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
-                   uint8_t* ws, const PrefillWs& P, uint16_t* out, void* stream) {
-  int rc = launch_route_generic(L, x, T, flags, R, ws, P, stream);
-  if (rc) return rc;
+                   uint8_t* ws, const PrefillWs& P, uint16_t* out, void* stream, uint32_t mask) {
+  if (mask & MOE_PREFILL_STAGE_ROUTE) {
+    const int rc = launch_route_generic(L, x, T, flags, R, ws, P, stream);
+    if (rc) return rc;
+  }
   hipStream_t s = (hipStream_t)stream;
   const int k = L->top_k, d = L->d, I = L->inter;
   const int Tk = T * k;
@@ -359,15 +353,16 @@ int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
   uint16_t* y = (uint16_t*)(ws + P.y);
   const int32_t* tiles = (const int32_t*)(ws + P.tiles);
   const int32_t* ctrl = (const int32_t*)(ws + P.ctrl);
-  {
+  if (mask & MOE_PREFILL_STAGE_STAGE_X) {
     const long pairs = (long)T * (d / 32);
     const int blocks = (int)min(4096L, (pairs + 7) / 8);
     hipLaunchKernelGGL(k_stage, dim3(blocks), dim3(256), 0, s, x, T, d, xs, xsum);
   }
   const ProjDesc pg = proj_pf(L, 0), pu = proj_pf(L, 1), pdn = proj_pf(L, 2);
   dim3 g1(P.max_tiles, I / 128);
+  if (mask & MOE_PREFILL_STAGE_GATEUP) {
   const bool g3 = L->q_gate == MOE_Q_INT3, u3 = L->q_up == MOE_Q_INT3;
-  const bool same = L->q_gate == L->q_up;
+  const bool same = L->q_gate == L->q_up;  // same correction operand
   if (g3 && u3)
     launch_gu<true, true, true>(g1, s, L, pg, pu, tiles, ctrl, R->perm_tok, Tk, xs, xsum, hs, hsum);
   else if (g3)
@@ -378,21 +373,32 @@ int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
     launch_gu<false, false, true>(g1, s, L, pg, pu, tiles, ctrl, R->perm_tok, Tk, xs, xsum, hs, hsum);
   else
     launch_gu<false, false, false>(g1, s, L, pg, pu, tiles, ctrl, R->perm_tok, Tk, xs, xsum, hs, hsum);
+  }
   dim3 g2(P.max_tiles, d / 256);
-  if (L->q_down == MOE_Q_INT3)
+  if (!(mask & MOE_PREFILL_STAGE_DOWN)) {
+  } else if (L->q_down == MOE_Q_INT3)
     hipLaunchKernelGGL((k_pf_gemm<1, 4, true, true, true>), g2, dim3(256), 0, s,
                        (const uint8_t*)L->experts, L->expert_stride, (const uint8_t*)L->shared, pdn,
-                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hsum, I, d, corr_const(L->q_down),
-                       corr_const(L->q_down), y, (uint16_t*)nullptr);
+                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hsum, I, d, qtype_offset(L->q_down),
+                       qtype_offset(L->q_down), y, (uint16_t*)nullptr);
   else
     hipLaunchKernelGGL((k_pf_gemm<1, 4, false, false, true>), g2, dim3(256), 0, s,
                        (const uint8_t*)L->experts, L->expert_stride, (const uint8_t*)L->shared, pdn,
-                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hsum, I, d, corr_const(L->q_down),
-                       corr_const(L->q_down), y, (uint16_t*)nullptr);
+                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hsum, I, d, qtype_offset(L->q_down),
+                       qtype_offset(L->q_down), y, (uint16_t*)nullptr);
+  if (mask & MOE_PREFILL_STAGE_COMBINE) {
+    const int rc = launch_combine(y, T, d, k, L->n_shared, R->inv_row, R->topk_w, x,
+                                  (flags & MOE_ADD_RESIDUAL) ? 1 : 0, out, stream);
+    if (rc) return rc;
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_combine(const uint16_t* y, int T, int d, int k, int n_shared, const int32_t* inv_row,
+                   const float* w, const uint16_t* x, int residual, uint16_t* out, void* stream) {
   const long n = (long)T * (d / 8);
-  hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, T, d, k,
-                     L->n_shared, R->inv_row, R->topk_w, x, (flags & MOE_ADD_RESIDUAL) ? 1 : 0,
-                     out);
+  hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, y, T, d, k, n_shared, inv_row, w, x, residual, out);
   return (int)hipGetLastError();
 }
 

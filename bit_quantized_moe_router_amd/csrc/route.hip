@@ -17,8 +17,8 @@ namespace bqmoe {
 // Wave per expert, up to 8 tokens per block row (grid.y tiles the tokens).
 // Router weights are stored [E][d] so a wave streams one contiguous row.
 // With `xs` set (decode), blocks also stage x for the expert kernels:
-// xs = x/16 (exact) and, per 32-group, the sum of x split into three bf16
-// parts (negated) for the matrix-core correction term.
+// xs = x/16 (exact) and, per 32-group, the sums W and S of the correction
+// term (see stage_sums in device_common.h).
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x, int T, int d,
                                                        int E, const float* __restrict__ Wr,
                                                        const float* __restrict__ bias,
@@ -68,20 +68,13 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
       const uint32_t xb = x[(size_t)t * d + g * 32 + j];
       const float xf = bf16_to_f32(xb);
       xs[(size_t)t * d + g * 32 + j] = (uint16_t)f32_to_bf16(xf * 0.0625f);
-      float s = xf;
+      float sw = xf * slot_weight(j), s = xf;
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
-      if (j == 0) {
-        const uint32_t hi = f32_to_bf16(s);
-        const float r1 = s - bf16_to_f32(hi);
-        const uint32_t mid = f32_to_bf16(r1);
-        const float r2 = r1 - bf16_to_f32(mid);
-        const uint32_t lo = f32_to_bf16(r2);
-        uint2 v;
-        v.x = ((hi ^ 0x8000u) & 0xFFFFu) | (((mid ^ 0x8000u) & 0xFFFFu) << 16);
-        v.y = (lo ^ 0x8000u) & 0xFFFFu;
-        *reinterpret_cast<uint2*>(xsum + ((size_t)t * G + g) * 4) = v;
+      for (int o = 16; o > 0; o >>= 1) {
+        sw += __shfl_xor(sw, o, 32);
+        s += __shfl_xor(s, o, 32);
       }
+      if (j == 0) *reinterpret_cast<uint4*>(xsum + ((size_t)t * G + g) * 8) = stage_sums(sw, s);
     }
   }
 }
@@ -215,8 +208,7 @@ __device__ int block_exclusive_scan(int* a, int n, int* wave_tot) {
 // One block of 512 threads for T <= 8 tokens: top-k per token (wave t), the
 // stable permutation of the T*k <= 64 rows (one wave, ballot matching), the
 // prefix sum over experts, and the list of active experts ("slots") in
-// ascending expert id followed by the shared expert.  Also clears the
-// combine counters of the down-projection kernel.
+// ascending expert id followed by the shared expert.
 __global__ __launch_bounds__(512) void k_dec_select(const float* __restrict__ logits, int T, int E,
                                                     int k, int n_shared, int32_t* __restrict__ ids,
                                                     float* __restrict__ wts,
@@ -224,8 +216,7 @@ __global__ __launch_bounds__(512) void k_dec_select(const float* __restrict__ lo
                                                     int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ perm_tok,
                                                     int32_t* __restrict__ inv_row,
-                                                    int32_t* __restrict__ slots,
-                                                    uint32_t* __restrict__ counters, int n_counters) {
+                                                    int32_t* __restrict__ slots) {
   __shared__ int s_ids[64];
   __shared__ int s_rank[64];
   __shared__ int s_cnt[MOE_MAX_EXPERTS];
@@ -233,7 +224,6 @@ __global__ __launch_bounds__(512) void k_dec_select(const float* __restrict__ lo
   __shared__ int s_flag[MOE_MAX_EXPERTS];
   __shared__ int s_tot[17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < n_counters; i += blockDim.x) counters[i] = 0u;
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
   if (wave < T) {
     int id;
@@ -270,28 +260,31 @@ __global__ __launch_bounds__(512) void k_dec_select(const float* __restrict__ lo
     counts[e] = s_cnt[e];
     offsets[e] = s_off[e];
     if (s_cnt[e] > 0) {
-      const int s = s_flag[e];
-      slots[1 + 3 * s] = e;
-      slots[2 + 3 * s] = s_off[e];
-      slots[3 + 3 * s] = s_cnt[e];
+      int32_t* rec = slots + kSlotRec * (1 + s_flag[e]);
+      rec[0] = e;
+      rec[1] = s_off[e];
+      rec[2] = s_cnt[e];
     }
   }
   if (tid == 0) {
     offsets[E] = total;
-    int ns = n_active;
-    if (n_shared) {
-      slots[1 + 3 * ns] = -1;
-      slots[2 + 3 * ns] = rows;
-      slots[3 + 3 * ns] = T;
-      ++ns;
+    slots[0] = n_active + (n_shared ? 1 : 0);
+  }
+  if (n_shared && tid < T) {  // shared slot: rows T*k + t, token t
+    int32_t* rec = slots + kSlotRec * (1 + n_active);
+    if (tid == 0) {
+      rec[0] = -1;
+      rec[1] = rows;
+      rec[2] = T;
     }
-    slots[0] = ns;
+    rec[kSlotTok + tid] = tid;
   }
   if (tid < rows) {
     const int e = s_ids[tid];
     const int pos = s_off[e] + s_rank[tid];
     perm_tok[pos] = tid / k;
     inv_row[tid] = pos;
+    slots[kSlotRec * (1 + s_flag[e]) + kSlotTok + s_rank[tid]] = tid / k;
   }
 }
 
@@ -443,17 +436,21 @@ int launch_route_generic(const moe_layer* L, const uint16_t* x, int T, uint32_t 
 
 // decode routing: logits + staging, then select (2 launches)
 int launch_decode_route(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
-                        moe_routing* R, uint8_t* ws, const DecodeWs& W, void* stream) {
+                        moe_routing* R, uint8_t* ws, const DecodeWs& W, void* stream,
+                        uint32_t mask) {
   hipStream_t s = (hipStream_t)stream;
   const int E = L->n_experts, k = L->top_k, d = L->d;
   const int do_logits = !(flags & MOE_LOGITS_GIVEN);
-  dim3 grid(max((E + 3) / 4, 64), 1);
-  hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
-                     L->router_bias, R->logits, do_logits, (uint16_t*)(ws + W.xs),
-                     (uint16_t*)(ws + W.xsum));
-  hipLaunchKernelGGL(k_dec_select, dim3(1), dim3(512), 0, s, R->logits, T, E, k, L->n_shared,
-                     R->topk_ids, R->topk_w, R->counts, R->offsets, R->perm_tok, R->inv_row,
-                     (int32_t*)(ws + W.slots), (uint32_t*)(ws + W.counters), d / 64);
+  if (mask & MOE_DECODE_STAGE_ROUTE) {
+    dim3 grid(max((E + 3) / 4, 64), 1);
+    hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
+                       L->router_bias, R->logits, do_logits, (uint16_t*)(ws + W.xs),
+                       (uint16_t*)(ws + W.xsum));
+  }
+  if (mask & MOE_DECODE_STAGE_SELECT)
+    hipLaunchKernelGGL(k_dec_select, dim3(1), dim3(512), 0, s, R->logits, T, E, k, L->n_shared,
+                       R->topk_ids, R->topk_w, R->counts, R->offsets, R->perm_tok, R->inv_row,
+                       (int32_t*)(ws + W.slots));
   return (int)hipGetLastError();
 }
 

@@ -160,6 +160,37 @@ moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T,
                                moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out,
                                void* stream);
 
+/* ---------------------------------------------------------------- stages
+ * Each forward call above enqueues a fixed sequence of kernels.  The _stages
+ * variants enqueue only the kernels whose bit is set in stage_mask, with the
+ * same arguments and validation; a stage reads what the earlier stages of the
+ * same call left in the workspace (and in R), so a stage may be run alone only
+ * after the earlier stages have run on that workspace with the same inputs.
+ * This is the hook used to time one kernel with events or a profiler, and
+ * running the stages in order one call at a time is equivalent to the full
+ * call.  An empty or unknown mask returns MOE_ERR_INVALID_ARG. */
+enum {
+  MOE_DECODE_STAGE_ROUTE = 1u,   /* router logits + activation staging */
+  MOE_DECODE_STAGE_SELECT = 2u,  /* top-k, weights, permutation, active-expert list */
+  MOE_DECODE_STAGE_GATEUP = 4u,  /* gate/up projections + SiLU gating */
+  MOE_DECODE_STAGE_DOWN = 8u,    /* down projection + weighted combine */
+  MOE_DECODE_STAGES_ALL = 15u
+};
+enum {
+  MOE_PREFILL_STAGE_ROUTE = 1u,    /* logits (unless given), top-k, permutation, tile list */
+  MOE_PREFILL_STAGE_STAGE_X = 2u,  /* activation staging */
+  MOE_PREFILL_STAGE_GATEUP = 4u,   /* grouped GEMM gate/up + SiLU gating */
+  MOE_PREFILL_STAGE_DOWN = 8u,     /* grouped GEMM down */
+  MOE_PREFILL_STAGE_COMBINE = 16u, /* unpermute + weighted combine */
+  MOE_PREFILL_STAGES_ALL = 31u
+};
+moe_status moe_forward_decode_stages(const moe_layer* L, const uint16_t* x, int32_t T,
+                                     uint32_t flags, moe_routing* R, void* ws, size_t ws_bytes,
+                                     uint16_t* out, uint32_t stage_mask, void* stream);
+moe_status moe_forward_prefill_stages(const moe_layer* L, const uint16_t* x, int32_t T,
+                                      uint32_t flags, moe_routing* R, void* ws, size_t ws_bytes,
+                                      uint16_t* out, uint32_t stage_mask, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 

@@ -183,3 +183,18 @@ def test_workspace_bytes():
     assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
     assert lib.moe_workspace_bytes(ctypes.byref(_layer(d=100).c), 4) == 0
     assert lib.moe_workspace_bytes(ctypes.byref(L.c), -1) == 0
+
+
+def test_stage_masks_are_checked():
+    lib = bq.load()
+    L = _layer()
+    R = _routing()
+    ws_bytes = lib.moe_workspace_bytes(ctypes.byref(L.c), 2)
+    for fn, allm in (("moe_forward_decode_stages", 15), ("moe_forward_prefill_stages", 31)):
+        f = getattr(lib, fn)
+        for bad in (0, allm + 1, 1 << 8):
+            assert f(ctypes.byref(L.c), FAKE, 2, 0, ctypes.byref(R), FAKE, ws_bytes,
+                     FAKE + (1 << 30), bad, None) == bq.MOE_ERR_INVALID_ARG
+        # a valid mask goes on to the ordinary argument checks
+        assert f(ctypes.byref(L.c), FAKE, 2, 0x80, ctypes.byref(R), FAKE, ws_bytes,
+                 FAKE + (1 << 30), 1, None) == bq.MOE_ERR_INVALID_ARG
