@@ -87,12 +87,170 @@ __host__ __device__ constexpr int dw_bytes(int M, int kbw) {
   return dw_rows_bytes(M, kbw) + dw_sum_bytes(M, kbw);
 }
 
+// ---------------------------------------------------------------- wave steps
+// 1. A wave's slice of its slot's M rows (k-blocks kb0 .. kb0+nkb of each row)
+//    and of their staged sums -> the wave's LDS region, by direct loads of
+//    1 KB each.  Row c of the slot is source row `base + c`, or with `gather`
+//    token (tok3 >> 3c) & 7 (decode tokens are < 8; no indexed array, which
+//    the compiler would place in scratch memory).  A lane whose bytes fall in
+//    a row's padding, past the slice or past the last row copies the first
+//    bytes of row 0 (never read).
+__device__ __forceinline__ int dec_src_row(int c, bool gather, int base, uint32_t tok3) {
+  return gather ? (int)((tok3 >> (3 * c)) & 7u) : base + c;
+}
+
+template <int KBW>
+__device__ __forceinline__ void dec_stage_rows(uint8_t* sA, uint8_t* sS, int lane, int M,
+                                               bool gather, int base, uint32_t tok3,
+                                               const uint16_t* __restrict__ A,
+                                               const uint8_t* __restrict__ Asum, int K, int kb0,
+                                               int nkb) {
+  constexpr int RS = dw_row_stride(KBW), SS = KBW * 64;
+  const int G = K / 32;
+  const int n_a = dw_rows_bytes(M, KBW) / 1024;
+  for (int i = 0; i < n_a; ++i) {
+    const int off = i * 1024 + lane * 16;
+    int c = off / RS;
+    const int within = off % RS;
+    const bool ok = c < M && within < nkb * 256;
+    c = ok ? c : 0;
+    const int src = dec_src_row(c, gather, base, tok3);
+    const uint8_t* g =
+        reinterpret_cast<const uint8_t*>(A + (size_t)src * K) + (ok ? kb0 * 256 + within : 0);
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(sA + i * 1024), 16, 0, 0);
+  }
+  const int n_s = dw_sum_bytes(M, KBW) / 1024;
+  for (int i = 0; i < n_s; ++i) {
+    const int off = i * 1024 + lane * 16;
+    int c = off / SS;
+    const int within = off % SS;
+    const bool ok = c < M && within < nkb * 64;
+    c = ok ? c : 0;
+    const int src = dec_src_row(c, gather, base, tok3);
+    const uint8_t* g = Asum + (size_t)src * G * 16 + (ok ? kb0 * 64 + within : 0);
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(sS + i * 1024), 16, 0, 0);
+  }
+}
+
+// 2. Packed tiles of a wave's k-blocks for NS streams: codes (8 B / lane),
+//    level bit 2 (4 B / lane, 3-bit only), scales of row r, groups q & 2 and
+//    (q & 2) + 1 (4 B / lane).  Stream j reads n-tile nt[j] of projection
+//    second(j) = (GATEUP && j == 1).  The loads are unconditional (a wave past
+//    the last k-block re-reads the last tile) so that their number is the
+//    compile-time constant dec_tile_loads().
+template <int NS, bool GATEUP, bool QA3, bool QB3>
+__host__ __device__ constexpr int dec_tile_loads(int kbw) {
+  return kbw * ((2 + (QA3 ? 1 : 0)) + (NS - 1) * (2 + ((GATEUP ? QB3 : QA3) ? 1 : 0)));
+}
+
+template <int NS, bool GATEUP, bool QA3, bool QB3, int KBW>
+__device__ __forceinline__ void dec_load_tiles(u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS],
+                                               uint32_t (&ws)[KBW][NS],
+                                               const uint8_t* const (&code_base)[2],
+                                               const size_t (&plane1)[2],
+                                               const size_t (&scale_off)[2],
+                                               const int (&nt)[NS], int KB, int kb0, int lane) {
+  const int q = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    const int kbc = min(kb0 + i, KB - 1);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int second = GATEUP && j == 1;
+      const bool q3 = second ? QB3 : QA3;
+      const uint8_t* base = code_base[second];
+      const size_t tile = (size_t)nt[j] * KB + kbc;
+      wc[i][j] = *reinterpret_cast<const u32x2*>(base + tile * 512 + lane * 8);
+      wh[i][j] = q3 ? *reinterpret_cast<const uint32_t*>(base + plane1[second] + tile * 256 +
+                                                         lane * 4)
+                    : 0u;
+      ws[i][j] = *reinterpret_cast<const uint32_t*>(base + scale_off[second] + tile * 128 +
+                                                    (r * 4 + (q & 2)) * 2);
+    }
+  }
+}
+
+// 3. Wait until at most N vector-memory loads are outstanding.  Loads complete
+//    in issue order, so with the N tile loads issued after the copies into
+//    LDS, the copies have landed.
+template <int N>
+__device__ __forceinline__ void wait_for_copies() {
+  static_assert(N <= 63, "vmcnt holds at most 63 outstanding loads");
+  __builtin_amdgcn_sched_barrier(0);
+  // s_waitcnt vmcnt(N), expcnt and lgkmcnt at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// (Wa, Sa, Wb, Sb): fp32 sums of h over the two 16-column halves of each
+// 32-group -> staged sums of the group, in place (down projection)
+template <int KBW>
+__device__ __forceinline__ void dec_half_sums_to_staged(uint8_t* sS, int lane, int M, int nkb) {
+  constexpr int SS = KBW * 64;
+  for (int t = lane; t < M * KBW * 4; t += 64) {
+    const int m = t / (KBW * 4), g = t % (KBW * 4);
+    if (g < nkb * 4) {
+      uint8_t* p = sS + m * SS + g * 16;
+      const float4 v = *reinterpret_cast<const float4*>(p);
+      *reinterpret_cast<uint4*>(p) = stage_sums(v.x + v.z, v.y + v.w);
+    }
+  }
+}
+
+// 4. Matrix-core work over a wave's k-blocks; per 32-group one correction op
+//    (two if the projections differ) and one op per stream; the group's scale
+//    multiplies MR accumulator rows (rows 4*(lane/16) + i carry real rows for
+//    i < M; MR = 1 when M == 1).
+template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int MR>
+__device__ __forceinline__ void dec_mfma(f32x4 (&acc)[NS], const u32x2 (&wc)[KBW][NS],
+                                         const uint32_t (&wh)[KBW][NS],
+                                         const uint32_t (&ws)[KBW][NS], int nkb,
+                                         const uint8_t* aptr, const uint8_t* sptr, u32x4 bca,
+                                         u32x4 bcb, const Unpack2R& ur, int r) {
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    if (i < nkb) {
+#pragma unroll
+      for (int GB = 0; GB < 4; ++GB) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(aptr + (i * 128 + GB * 32) * 2);
+        const u32x4 sv = *reinterpret_cast<const u32x4*>(sptr + (i * 4 + GB) * 16);
+        const f32x4 corr_a = mfma_corr(sv, bca);
+        f32x4 corr_b = corr_a;
+        if constexpr (!SAMEC) corr_b = mfma_corr(sv, bcb);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const bool second = GATEUP && j == 1;
+          const bool q3 = second ? QB3 : QA3;
+          const uint32_t word = (GB < 2) ? wc[i][j][0] : wc[i][j][1];
+          u32x4 b;
+          if (q3) {
+            if (GB == 0) b = unpack3<0>(word, wh[i][j]);
+            if (GB == 1) b = unpack3<1>(word, wh[i][j]);
+            if (GB == 2) b = unpack3<2>(word, wh[i][j]);
+            if (GB == 3) b = unpack3<3>(word, wh[i][j]);
+          } else {
+            b = (GB & 1) ? unpack2_r<1>(word, ur) : unpack2_r<0>(word, ur);
+          }
+          const f32x4 dd = mfma32(a, b, second ? corr_b : corr_a);
+          // lane GB*16 + r holds scales (r, GB & 2) and (r, (GB & 2) + 1)
+          const uint32_t sw = (uint32_t)__shfl((int)ws[i][j], GB * 16 + r, 64);
+          const float s = f16_to_f32((GB & 1) ? (sw >> 16) : sw);
+#pragma unroll
+          for (int m = 0; m < MR; ++m) acc[j][m] = fmaf(s, dd[m], acc[j][m]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- projection kernel
 // GATEUP = true: streams 0 (gate) and 1 (up) of n-tile blockIdx % groups;
 //   epilogue h = bf16(SiLU(g) * u), stored as h/16, plus fp32 (W, S) sums of
 //   h over the tile's 16 columns (half of a 32-group of the down projection).
 // GATEUP = false (down): streams 0..3 = n-tiles 4g .. 4g+3; the 32-group sums
 //   of h are the two half sums added; epilogue y = bf16(acc).
-template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KSPLIT, int KBW>
+// ONE_ROW: launched for a single token, so every slot has M == 1.
+template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KSPLIT, int KBW, bool ONE_ROW>
 __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ slots, const uint16_t* __restrict__ A,
@@ -102,164 +260,59 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int groups = N / (16 * (GATEUP ? 1 : 4));
   const int slot = blockIdx.x / groups, grp = blockIdx.x % groups;
-  if (slot >= slots[0]) return;
   // the slot record is uniform: scalar loads, which do not wait behind the
-  // packed-tile loads below
+  // packed-tile loads below; records past the last slot have M == 0
   const int32_t* rec = slots + kSlotRec * (1 + slot);
   const int e = rec[0], row0 = rec[1], M = rec[2];
-  int src_row[kDecMaxRows];
+  if (M == 0) return;
+  uint32_t tok3 = 0;  // tokens of the slot's rows, 3 bits each
+  if (GATEUP) {
 #pragma unroll
-  for (int c = 0; c < kDecMaxRows; ++c)
-    src_row[c] = GATEUP ? (c < M ? rec[kSlotTok + c] : rec[kSlotTok]) : row0 + (c < M ? c : 0);
+    for (int c = 0; c < kDecMaxRows; ++c)
+      tok3 |= c < M ? (uint32_t)rec[kSlotTok + c] << (3 * c) : 0u;
+  }
   const uint8_t* blob = e >= 0 ? experts + (size_t)e * stride : shared;
   // projection offsets in registers before any LDS write (which the compiler
   // cannot tell apart from the argument memory)
-  const uint8_t* code_base[2] = {blob + pa.off, blob + pb.off};
+  const uint8_t* const code_base[2] = {blob + pa.off, blob + pb.off};
   const size_t plane1[2] = {pa.plane1, pb.plane1};
   const size_t scale_off[2] = {pa.scales, pb.scales};
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int KB = K / 128, G = K / 32;
+  const int KB = K / 128;
   const int per = (KB + KSPLIT - 1) / KSPLIT;
   const int kb0 = min(KB, wave * per);
   const int nkb = min(KB, kb0 + per) - kb0;  // 0 .. KBW
-  constexpr int RS = dw_row_stride(KBW), SS = KBW * 64;
   uint8_t* sA = lds + wave * dw_bytes(Mmax, KBW);
   uint8_t* sS = sA + dw_rows_bytes(Mmax, KBW);
 
-  // 1. this wave's slice of the rows and sums -> its LDS region.  A lane
-  //    whose bytes fall in a row's padding, past the slice or past the last
-  //    row copies the first bytes of row 0 (never read back).
-  {
-    const int n_a = dw_rows_bytes(M, KBW) / 1024;
-    for (int i = 0; i < n_a; ++i) {
-      const int off = i * 1024 + lane * 16;
-      int c = off / RS;
-      const int within = off % RS;
-      const bool ok = c < M && within < nkb * 256;
-      c = ok ? c : 0;
-      int src = src_row[0];
-#pragma unroll
-      for (int cc = 1; cc < kDecMaxRows; ++cc) src = c == cc ? src_row[cc] : src;
-      const uint8_t* g = reinterpret_cast<const uint8_t*>(A + (size_t)src * K) +
-                         (ok ? kb0 * 256 + within : 0);
-      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(sA + i * 1024), 16, 0, 0);
-    }
-    const int n_s = dw_sum_bytes(M, KBW) / 1024;
-    for (int i = 0; i < n_s; ++i) {
-      const int off = i * 1024 + lane * 16;
-      int c = off / SS;
-      const int within = off % SS;
-      const bool ok = c < M && within < nkb * 64;
-      c = ok ? c : 0;
-      int src = src_row[0];
-#pragma unroll
-      for (int cc = 1; cc < kDecMaxRows; ++cc) src = c == cc ? src_row[cc] : src;
-      const uint8_t* g = Asum + (size_t)src * G * 16 + (ok ? kb0 * 64 + within : 0);
-      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(sS + i * 1024), 16, 0, 0);
-    }
-  }
+  dec_stage_rows<KBW>(sA, sS, lane, M, GATEUP, row0, tok3, A, Asum, K, kb0, nkb);
   __builtin_amdgcn_sched_barrier(0);
-
-  // 2. packed tiles of this wave's k-blocks: codes (8 B / lane), level bit 2
-  //    (4 B / lane, 3-bit only), scales of row r, groups q & 2 and (q & 2) + 1
-  //    (4 B / lane).  The
-  //    loads are unconditional (a wave past the last k-block re-reads the last
-  //    tile) so that their number is a compile-time constant.
-  const int nt0 = GATEUP ? grp : grp * 4;
+  int nt[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) nt[j] = GATEUP ? grp : grp * 4 + j;
   u32x2 wc[KBW][NS];
   uint32_t wh[KBW][NS], ws[KBW][NS];
-#pragma unroll
-  for (int i = 0; i < KBW; ++i) {
-    const int kbc = min(kb0 + i, KB - 1);
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int second = GATEUP && j == 1;
-      const bool q3 = second ? QB3 : QA3;
-      const uint8_t* base = code_base[second];
-      const size_t tile = (size_t)(GATEUP ? nt0 : nt0 + j) * KB + kbc;
-      wc[i][j] = *reinterpret_cast<const u32x2*>(base + tile * 512 + lane * 8);
-      wh[i][j] = q3 ? *reinterpret_cast<const uint32_t*>(base + plane1[second] + tile * 256 +
-                                                         lane * 4)
-                    : 0u;
-      ws[i][j] = *reinterpret_cast<const uint32_t*>(base + scale_off[second] + tile * 128 +
-                                                    (r * 4 + (q & 2)) * 2);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // 3. vector-memory loads complete in issue order: with only the tile loads
-  //    outstanding, this wave's copies into LDS have landed.
-  constexpr int kTileLoads = KBW * ((2 + (QA3 ? 1 : 0)) + (NS - 1) * (2 + (QB3 ? 1 : 0)));
-  static_assert(kTileLoads <= 63, "vmcnt holds at most 63 outstanding loads");
-  // s_waitcnt vmcnt(kTileLoads), expcnt and lgkmcnt at their maxima (no wait)
-  __builtin_amdgcn_s_waitcnt((kTileLoads & 15) | ((kTileLoads >> 4) << 14) | (7 << 4) | (15 << 8));
-  __builtin_amdgcn_sched_barrier(0);
+  dec_load_tiles<NS, GATEUP, QA3, QB3, KBW>(wc, wh, ws, code_base, plane1, scale_off, nt, KB,
+                                            kb0, lane);
+  wait_for_copies<dec_tile_loads<NS, GATEUP, QA3, QB3>(KBW)>();
+  if constexpr (!GATEUP) dec_half_sums_to_staged<KBW>(sS, lane, M, nkb);
 
-  if constexpr (!GATEUP) {
-    // (Wa, Sa, Wb, Sb) fp32 half sums -> staged sums of the 32-group, in place
-    for (int t = lane; t < M * KBW * 4; t += 64) {
-      const int m = t / (KBW * 4), g = t % (KBW * 4);
-      if (g < nkb * 4) {
-        uint8_t* p = sS + m * SS + g * 16;
-        const float4 v = *reinterpret_cast<const float4*>(p);
-        *reinterpret_cast<uint4*>(p) = stage_sums(v.x + v.z, v.y + v.w);
-      }
-    }
-  }
-
-  // 4. matrix-core work
   const u32x4 bca = corr_b_operand(q == 0, QA3, ca);
   const u32x4 bcb = corr_b_operand(q == 0, QB3, cb);
   const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1), lane_copy(uk.b2)};
   const int arow = r < M ? r : 0;
-  const uint8_t* aptr = sA + arow * RS + q * 16;
-  const uint8_t* sptr = sS + arow * SS;
+  const uint8_t* aptr = sA + arow * dw_row_stride(KBW) + q * 16;
+  const uint8_t* sptr = sS + arow * KBW * 64;
   f32x4 acc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // MR accumulator rows per lane carry real rows: rows 4*(lane/16) + i, so
-  // with M == 1 only i = 0 does (and only in lanes 0..15)
-  auto work = [&](auto mr) {
-    constexpr int MR = decltype(mr)::value;
-#pragma unroll
-    for (int i = 0; i < KBW; ++i) {
-      if (i < nkb) {
-#pragma unroll
-        for (int GB = 0; GB < 4; ++GB) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(aptr + (i * 128 + GB * 32) * 2);
-          const u32x4 sv = *reinterpret_cast<const u32x4*>(sptr + (i * 4 + GB) * 16);
-          const f32x4 corr_a = mfma_corr(sv, bca);
-          f32x4 corr_b = corr_a;
-          if constexpr (!SAMEC) corr_b = mfma_corr(sv, bcb);
-#pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            const bool second = GATEUP && j == 1;
-            const bool q3 = second ? QB3 : QA3;
-            const uint32_t word = (GB < 2) ? wc[i][j][0] : wc[i][j][1];
-            u32x4 b;
-            if (q3) {
-              if (GB == 0) b = unpack3<0>(word, wh[i][j]);
-              if (GB == 1) b = unpack3<1>(word, wh[i][j]);
-              if (GB == 2) b = unpack3<2>(word, wh[i][j]);
-              if (GB == 3) b = unpack3<3>(word, wh[i][j]);
-            } else {
-              b = (GB & 1) ? unpack2_r<1>(word, ur) : unpack2_r<0>(word, ur);
-            }
-            const f32x4 dd = mfma32(a, b, second ? corr_b : corr_a);
-            // lane GB*16 + r holds scales (r, GB & 2) and (r, (GB & 2) + 1)
-            const uint32_t sw = (uint32_t)__shfl((int)ws[i][j], GB * 16 + r, 64);
-            const float s = f16_to_f32((GB & 1) ? (sw >> 16) : sw);
-#pragma unroll
-            for (int m = 0; m < MR; ++m) acc[j][m] = fmaf(s, dd[m], acc[j][m]);
-          }
-        }
-      }
-    }
-  };
-  if (M == 1)
-    work(std::integral_constant<int, 1>{});
+  if (ONE_ROW || M == 1)
+    dec_mfma<NS, GATEUP, QA3, QB3, SAMEC, KBW, 1>(acc, wc, wh, ws, nkb, aptr, sptr, bca, bcb, ur,
+                                                  r);
   else
-    work(std::integral_constant<int, 4>{});
+    dec_mfma<NS, GATEUP, QA3, QB3, SAMEC, KBW, 4>(acc, wc, wh, ws, nkb, aptr, sptr, bca, bcb, ur,
+                                                  r);
 
   // 5. cross-wave reduction in a fixed order (every wave is done with LDS)
   __syncthreads();
@@ -304,8 +357,92 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
       const int ln = 16 * (row >> 2) + col, i = row & 3;
       float s = 0.f;
       for (int w = 0; w < KSPLIT; ++w) s += red[((w * 4 + j) * 4 + i) * 32 + ln];
-      out[(size_t)(row0 + row) * N + (nt0 + j) * 16 + col] = (uint16_t)f32_to_bf16(s);
+      out[(size_t)(row0 + row) * N + (nt[0] + j) * 16 + col] = (uint16_t)f32_to_bf16(s);
     }
+  }
+}
+
+// ------------------------------------------------- down projection + combine
+// For few slots (<= 16) and a short reduction (I <= 2048): block = one
+// 16-column n-tile of the output, wave s = slot s over the whole of I (no
+// cross-wave reduction).  Each wave leaves y = bf16(h . Wd) of its rows for
+// the tile in LDS; the block then forms
+//   out[t] = bf16( [x[t]] + sum_j w[t][j] * y[inv_row[t][j]] + [y[T*k + t]] )
+// for its 16 columns in the same order as the separate combine kernel.
+template <bool Q3, int KBW, bool ONE_ROW>
+__global__ __launch_bounds__(1024) void k_dec_down_combine(
+    const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
+    ProjDesc pd, const int32_t* __restrict__ slots, int max_slots,
+    const uint16_t* __restrict__ hs, const uint8_t* __restrict__ hsum, int K, int N, int Mmax,
+    float cd, Unpack2K uk, int T, int k, int n_shared, const int32_t* __restrict__ inv_row,
+    const float* __restrict__ topk_w, const uint16_t* __restrict__ x, int residual,
+    uint16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int nwaves = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nt = blockIdx.x;
+  const int rows_total = T * k + T * n_shared;
+  float* ylds = reinterpret_cast<float*>(lds + nwaves * dw_bytes(Mmax, KBW));  // [rows][16]
+  int* s_inv = reinterpret_cast<int*>(ylds + rows_total * 16);
+  float* s_w = reinterpret_cast<float*>(s_inv + kDecodeMaxRoutedRows);
+  // the combine's inputs, loaded first (they are long complete when used)
+  int my_inv = 0;
+  float my_w = 0.f, my_x = 0.f;
+  if (tid < T * k) {
+    my_inv = inv_row[tid];
+    my_w = topk_w[tid];
+  }
+  if (tid < T * 16 && residual) my_x = bf16_to_f32(x[(size_t)(tid >> 4) * N + nt * 16 + (tid & 15)]);
+  const int32_t* rec = slots + kSlotRec * (1 + (wave < max_slots ? wave : 0));
+  const int e = rec[0], row0 = rec[1], M = wave < max_slots ? rec[2] : 0;
+  if (M > 0) {
+    const uint8_t* blob = e >= 0 ? experts + (size_t)e * stride : shared;
+    const uint8_t* const code_base[2] = {blob + pd.off, blob + pd.off};
+    const size_t plane1[2] = {pd.plane1, pd.plane1};
+    const size_t scale_off[2] = {pd.scales, pd.scales};
+    const int KB = K / 128;
+    uint8_t* sA = lds + wave * dw_bytes(Mmax, KBW);
+    uint8_t* sS = sA + dw_rows_bytes(Mmax, KBW);
+    dec_stage_rows<KBW>(sA, sS, lane, M, false, row0, 0u, hs, hsum, K, 0, KB);
+    __builtin_amdgcn_sched_barrier(0);
+    const int ntl[1] = {nt};
+    u32x2 wc[KBW][1];
+    uint32_t wh[KBW][1], ws[KBW][1];
+    dec_load_tiles<1, false, Q3, Q3, KBW>(wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0,
+                                          lane);
+    wait_for_copies<dec_tile_loads<1, false, Q3, Q3>(KBW)>();
+    dec_half_sums_to_staged<KBW>(sS, lane, M, KB);
+    const u32x4 bc = corr_b_operand(q == 0, Q3, cd);
+    const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1),
+                         lane_copy(uk.b2)};
+    const int arow = r < M ? r : 0;
+    const uint8_t* aptr = sA + arow * dw_row_stride(KBW) + q * 16;
+    const uint8_t* sptr = sS + arow * KBW * 64;
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (ONE_ROW || M == 1)
+      dec_mfma<1, false, Q3, Q3, true, KBW, 1>(acc, wc, wh, ws, KB, aptr, sptr, bc, bc, ur, r);
+    else
+      dec_mfma<1, false, Q3, Q3, true, KBW, 4>(acc, wc, wh, ws, KB, aptr, sptr, bc, bc, ur, r);
+    // rows 4*(lane/16) + i, column lane % 16 -> y of permuted row row0 + row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (lane >> 4) + i;
+      if (lane < 32 && row < M) ylds[(row0 + row) * 16 + r] = bf16_to_f32(f32_to_bf16(acc[0][i]));
+    }
+  }
+  if (tid < T * k) {
+    s_inv[tid] = my_inv;
+    s_w[tid] = my_w;
+  }
+  __syncthreads();
+  // weighted combine of this tile's 16 columns, one thread per (token, column)
+  if (tid < T * 16) {
+    const int t = tid >> 4, col = tid & 15;
+    float a = my_x;
+    for (int j = 0; j < k; ++j) a = fmaf(s_w[t * k + j], ylds[s_inv[t * k + j] * 16 + col], a);
+    if (n_shared) a += ylds[(T * k + t) * 16 + col];
+    out[(size_t)t * N + nt * 16 + col] = (uint16_t)f32_to_bf16(a);
   }
 }
 
@@ -362,17 +499,50 @@ bool decode_shape_ok(const moe_layer* L, int T) {
          dec_lds_bytes(false, dn, Mmax) <= kLdsLimit;
 }
 
+// Fused down projection + combine: at most 16 slots (one wave each) and
+// I <= 2048 (16 k-blocks per wave).
+static int dc_waves(int T, int max_slots) {
+  const int need = (T * 16 + 63) / 64;  // the combine's (token, column) threads
+  return max_slots > need ? max_slots : need;
+}
+
+static int dc_kbw(int I) {
+  const int KB = I / 128;
+  int kbw = 2;
+  while (kbw < KB) kbw *= 2;
+  return kbw;
+}
+
+static size_t dc_lds_bytes(const moe_layer* L, int T, int max_slots, int Mmax) {
+  const int waves = dc_waves(T, max_slots);
+  const int rows = T * L->top_k + T * L->n_shared;
+  return (size_t)waves * dw_bytes(Mmax, dc_kbw(L->inter)) + (size_t)rows * 16 * 4 +
+         (size_t)kDecodeMaxRoutedRows * 8;
+}
+
+static bool dc_ok(const moe_layer* L, int T, int max_slots, int Mmax) {
+  return max_slots <= 16 && L->inter <= 2048 && dc_lds_bytes(L, T, max_slots, Mmax) <= kLdsLimit;
+}
+
 template <bool GATEUP, bool QA3, bool QB3, bool SAMEC>
 static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const moe_layer* L,
                        ProjDesc pa, ProjDesc pb, const int32_t* slots, const uint16_t* A,
                        const uint8_t* Asum, int K, int N, float ca, float cb, uint16_t* out,
                        float* psum) {
   const size_t lds = dec_lds_bytes(GATEUP, sh, Mmax);
-#define BQ_L(KS, KBW)                                                                       \
-  hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW>), dim3(n_blocks),        \
-                     dim3(64 * KS), lds, s, (const uint8_t*)L->experts, L->expert_stride,   \
-                     (const uint8_t*)L->shared, pa, pb, slots, A, Asum, K, N, Mmax, ca, cb, \
-                     out, psum, kUnpack2)
+#define BQ_L(KS, KBW)                                                                         \
+  do {                                                                                        \
+    if (Mmax == 1)                                                                            \
+      hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, true>), dim3(n_blocks), \
+                         dim3(64 * KS), lds, s, (const uint8_t*)L->experts, L->expert_stride, \
+                         (const uint8_t*)L->shared, pa, pb, slots, A, Asum, K, N, Mmax, ca,   \
+                         cb, out, psum, kUnpack2);                                            \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, false>),               \
+                         dim3(n_blocks), dim3(64 * KS), lds, s, (const uint8_t*)L->experts,   \
+                         L->expert_stride, (const uint8_t*)L->shared, pa, pb, slots, A, Asum, \
+                         K, N, Mmax, ca, cb, out, psum, kUnpack2);                            \
+  } while (0)
   if (sh.ksplit == 4 && sh.kbw == 2)
     BQ_L(4, 2);
   else if (sh.ksplit == 4 && sh.kbw == 4)
@@ -432,7 +602,46 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
 #undef BQ_GU
     if (rc) return rc;
   }
-  if (mask & MOE_DECODE_STAGE_DOWN) {
+  if ((mask & MOE_DECODE_STAGE_DOWN) && dc_ok(L, T, W.max_slots, Mmax)) {
+    const ProjDesc pd = proj(L, 2);
+    const int waves = dc_waves(T, W.max_slots), kbw = dc_kbw(I);
+    const size_t lds = dc_lds_bytes(L, T, W.max_slots, Mmax);
+    const float cd = qtype_offset(L->q_down);
+    const uint8_t* hsb = (const uint8_t*)hsum;
+    const int res = (flags & MOE_ADD_RESIDUAL) ? 1 : 0;
+#define BQ_DC(Q3, KBW)                                                                         \
+  do {                                                                                         \
+    if (Mmax == 1)                                                                             \
+      hipLaunchKernelGGL((k_dec_down_combine<Q3, KBW, true>), dim3(d / 16), dim3(64 * waves),  \
+                         lds, s, (const uint8_t*)L->experts, L->expert_stride,                 \
+                         (const uint8_t*)L->shared, pd, slots, W.max_slots, hs, hsb, I, d,     \
+                         Mmax, cd, kUnpack2, T, k, L->n_shared, R->inv_row, R->topk_w, x, res, \
+                         out);                                                                 \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_dec_down_combine<Q3, KBW, false>), dim3(d / 16), dim3(64 * waves), \
+                         lds, s, (const uint8_t*)L->experts, L->expert_stride,                 \
+                         (const uint8_t*)L->shared, pd, slots, W.max_slots, hs, hsb, I, d,     \
+                         Mmax, cd, kUnpack2, T, k, L->n_shared, R->inv_row, R->topk_w, x, res, \
+                         out);                                                                 \
+  } while (0)
+#define BQ_DCQ(Q3)        \
+  do {                    \
+    if (kbw == 2)         \
+      BQ_DC(Q3, 2);       \
+    else if (kbw == 4)    \
+      BQ_DC(Q3, 4);       \
+    else if (kbw == 8)    \
+      BQ_DC(Q3, 8);       \
+    else                  \
+      BQ_DC(Q3, 16);      \
+  } while (0)
+    if (L->q_down == MOE_Q_INT3)
+      BQ_DCQ(true);
+    else
+      BQ_DCQ(false);
+#undef BQ_DCQ
+#undef BQ_DC
+  } else if (mask & MOE_DECODE_STAGE_DOWN) {
     const ProjDesc pd = proj(L, 2);
     const DecShape sh = dec_shape(false, I);
     const int nb = W.max_slots * (d / 64);

@@ -38,7 +38,8 @@ struct ProjDesc {
 // staged sums (W = sum x_k * base_k / 16, S = sum x_k).
 // Decode slot list: a 16-int header (n_slots first), then one 16-int record per
 // slot: expert (-1 = shared), first permuted row, row count M, unused, and the
-// token of each of the M rows.
+// token of each of the M rows.  All max_slots records are written; those past
+// the last slot have M == 0.
 constexpr int kSlotRec = 16;
 constexpr int kSlotTok = 4;
 constexpr int kDecodeMaxRoutedRows = 64;  // T*k for the decode path
@@ -47,7 +48,7 @@ constexpr int kDecodeMaxDim = 8192;       // d and inter for the decode path
 
 // Workspace layouts (byte offsets from the workspace base).
 struct DecodeWs {
-  size_t slots;     // int32 [1 + 3*max_slots]: n_slots, then (expert|-1, row0, rows)
+  size_t slots;     // int32 [16 * (1 + max_slots)]: header, then one record per slot
   size_t xs;        // bf16 [T][d]        x / 16
   size_t xsum;      // bf16 [T][d/32][8]  staged sums (W, S) of each 32-group of x
   size_t hs;        // bf16 [rows][I]     h / 16

@@ -283,15 +283,27 @@ __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = 0.f;
   }
-  for (int j = 0; j < k; ++j) {
-    const int rr = inv_row[(size_t)t * k + j];
-    const float wt = w[(size_t)t * k + j];
-    const uint4 yv = *reinterpret_cast<const uint4*>(y + (size_t)rr * d + c);
-    const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+  // rows in batches of 8: all of a batch's loads are in flight together
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    uint4 yv[8];
+    float wt[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[2 * i] = fmaf(wt, bf16_to_f32(yw[i] & 0xFFFFu), a[2 * i]);
-      a[2 * i + 1] = fmaf(wt, bf16_to_f32(yw[i] >> 16), a[2 * i + 1]);
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = min(j0 + jj, k - 1);
+      const int rr = inv_row[(size_t)t * k + j];
+      wt[jj] = j0 + jj < k ? w[(size_t)t * k + j] : 0.f;
+      yv[jj] = *reinterpret_cast<const uint4*>(y + (size_t)rr * d + c);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < k) {
+        const uint32_t yw[4] = {yv[jj].x, yv[jj].y, yv[jj].z, yv[jj].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[2 * i] = fmaf(wt[jj], bf16_to_f32(yw[i] & 0xFFFFu), a[2 * i]);
+          a[2 * i + 1] = fmaf(wt[jj], bf16_to_f32(yw[i] >> 16), a[2 * i + 1]);
+        }
+      }
     }
   }
   if (n_shared) {

@@ -79,9 +79,84 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   }
 }
 
-// candidate (va, ia) ranks before (vb, ib)
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+// Decode router logits (T <= 8): block per expert, its 4 waves split d and
+// issue all of their router-row loads at once (the row is read once for all
+// T tokens); partial sums meet in LDS.  The blocks also stage x for the
+// expert kernels: xs = x/16 (exact) and, per 32-group, the staged sums.
+__global__ __launch_bounds__(256) void k_dec_logits(const uint16_t* __restrict__ x, int T, int d,
+                                                    int E, const float* __restrict__ Wr,
+                                                    const float* __restrict__ bias,
+                                                    float* __restrict__ logits, int do_logits,
+                                                    uint16_t* __restrict__ xs,
+                                                    uint16_t* __restrict__ xsum) {
+  __shared__ float s_part[4][MOE_MAX_DECODE_TOKENS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int e = blockIdx.x;
+  if (do_logits && e < E) {
+    float acc[MOE_MAX_DECODE_TOKENS];
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) acc[t] = 0.f;
+    const float* w = Wr + (size_t)e * d;
+#pragma unroll 4
+    for (int i = tid * 4; i < d; i += 1024) {
+      const float4 wv = *reinterpret_cast<const float4*>(w + i);
+#pragma unroll
+      for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+        if (t < T) {
+          const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * d + i);
+          acc[t] = fmaf(bf16_to_f32(xv.x & 0xFFFFu), wv.x, acc[t]);
+          acc[t] = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc[t]);
+          acc[t] = fmaf(bf16_to_f32(xv.y & 0xFFFFu), wv.z, acc[t]);
+          acc[t] = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+      if (t < T) {
+        const float s = wave_sum(acc[t]);
+        if (lane == 0) s_part[wave][t] = s;
+      }
+    }
+    __syncthreads();
+    if (tid < T) {
+      const float s = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+      logits[(size_t)tid * E + e] = s + (bias ? bias[e] : 0.f);
+    }
+  }
+  // staging: one 32-lane half-wave per (token, group), spread over the grid
+  const int G = d / 32;
+  const int pairs = T * G;
+  const int half = tid >> 5, j = tid & 31;
+  for (int p = blockIdx.x * 8 + half; p < pairs; p += gridDim.x * 8) {
+    const int t = p / G, g = p % G;
+    const uint32_t xb = x[(size_t)t * d + g * 32 + j];
+    const float xf = bf16_to_f32(xb);
+    xs[(size_t)t * d + g * 32 + j] = (uint16_t)f32_to_bf16(xf * 0.0625f);
+    float sw = xf * slot_weight(j), sm = xf;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) {
+      sw += __shfl_xor(sw, o, 32);
+      sm += __shfl_xor(sm, o, 32);
+    }
+    if (j == 0) *reinterpret_cast<uint4*>(xsum + ((size_t)t * G + g) * 8) = stage_sums(sw, sm);
+  }
+}
+
+// Order-preserving integer key of a logit: a > b as floats iff key(a) >
+// key(b), -0 and +0 share a key (they compare equal), and NaN gets the lowest
+// key of all, so that ranking is a strict total order on (key, index) and
+// every selected id is a valid, distinct expert whatever the inputs.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;  // NaN
+  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;              // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// candidate (ka, ia) ranks before (kb, ib): larger key, then lower index
+__device__ __forceinline__ bool ranks_before(uint32_t ka, int ia, uint32_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
 }
 
 // Top-k of one token's E logits by one wave.  Lane l holds experts l + 64i.
@@ -90,11 +165,13 @@ __device__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, i
                           float& my_w) {
   constexpr int MAXPER = MOE_MAX_EXPERTS / 64;
   float v[MAXPER];
+  uint32_t key[MAXPER];
   const int per = (E + 63) / 64;
 #pragma unroll
   for (int i = 0; i < MAXPER; ++i) {
     const int e = lane + 64 * i;
     v[i] = (i < per && e < E) ? L[e] : -INFINITY;
+    key[i] = order_key(v[i]);
   }
   uint32_t taken = 0;  // bit i: v[i] already selected (or absent)
 #pragma unroll
@@ -104,13 +181,16 @@ __device__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, i
   my_id = -1;
   float my_v = 0.f;
   for (int j = 0; j < k; ++j) {
-    // lane-local best
+    // lane-local best (absent and taken entries never win; a present entry
+    // always beats the initial sentinel, NaN included)
+    uint32_t bk = 0u;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
       const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && ranks_before(v[i], e, bv, bi)) {
+      if (!((taken >> i) & 1u) && ranks_before(key[i], e, bk, bi)) {
+        bk = key[i];
         bv = v[i];
         bi = e;
       }
@@ -118,9 +198,11 @@ __device__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, i
     // wave argmax under the same rule
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t ok = __shfl_xor(bk, o, 64);
       const float ov = __shfl_xor(bv, o, 64);
       const int oi = __shfl_xor(bi, o, 64);
-      if (ranks_before(ov, oi, bv, bi)) {
+      if (ranks_before(ok, oi, bk, bi)) {
+        bk = ok;
         bv = ov;
         bi = oi;
       }
@@ -205,86 +287,162 @@ __device__ int block_exclusive_scan(int* a, int n, int* wave_tot) {
 }
 
 // ------------------------------------------------- decode: select + permute
-// One block of 512 threads for T <= 8 tokens: top-k per token (wave t), the
-// stable permutation of the T*k <= 64 rows (one wave, ballot matching), the
-// prefix sum over experts, and the list of active experts ("slots") in
-// ascending expert id followed by the shared expert.
-__global__ __launch_bounds__(512) void k_dec_select(const float* __restrict__ logits, int T, int E,
-                                                    int k, int n_shared, int32_t* __restrict__ ids,
-                                                    float* __restrict__ wts,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ perm_tok,
-                                                    int32_t* __restrict__ inv_row,
-                                                    int32_t* __restrict__ slots) {
-  __shared__ int s_ids[64];
-  __shared__ int s_rank[64];
-  __shared__ int s_cnt[MOE_MAX_EXPERTS];
-  __shared__ int s_off[MOE_MAX_EXPERTS];
-  __shared__ int s_flag[MOE_MAX_EXPERTS];
-  __shared__ int s_tot[17];
+// One block of 1024 threads for T <= 8 tokens (T*k <= 64 rows), built from
+// parallel counts rather than serial reductions:
+//   1. every logit's rank inside its token = the number of logits that rank
+//      before it (P threads per logit share the count); ranks below k are
+//      the selection, already in output order;
+//   2. the <= 64 selected rows sit one per lane of wave 0, which derives each
+//      row's in-expert rank, permuted position and slot from ~log2(E)
+//      ballots over the expert-id bits;
+//   3. every expert's count and offset is a count over the rows, held in
+//      registers.
+// Slots list the active experts in ascending id, then the shared expert.
+constexpr int kSelThreads = 1024;
+
+__device__ __forceinline__ float key_value(uint32_t key) {  // inverse of order_key
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_dec_select(
+    const float* __restrict__ logits, int T, int E, int k, int n_shared,
+    int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_tok, int32_t* __restrict__ inv_row,
+    int32_t* __restrict__ slots, int max_slots) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_key[MOE_MAX_DECODE_TOKENS * MOE_MAX_EXPERTS];
+  __shared__ __attribute__((aligned(16))) int s_row[kDecodeMaxRoutedRows];  // expert of row t*k + j
+  __shared__ float s_selv[kDecodeMaxRoutedRows];
+  __shared__ int s_nact;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
-  if (wave < T) {
-    int id;
-    float wt;
-    wave_topk(logits + (size_t)wave * E, E, k, lane, id, wt);
-    if (lane < k) {
-      ids[(size_t)wave * k + lane] = id;
-      wts[(size_t)wave * k + lane] = wt;
-      s_ids[wave * k + lane] = id;
+  const int n = T * E, rows = T * k;
+  for (int i = tid; i < n; i += kSelThreads) s_key[i] = order_key(logits[i]);
+  __syncthreads();
+  // 1. ranks; P consecutive lanes per logit, each counting over E/P of its row
+  int P = 1;
+  while (P < 16 && 2 * P * n <= kSelThreads) P *= 2;
+  const int chunk = (E + P - 1) / P;
+  for (int base = 0; base < n * P; base += kSelThreads) {
+    const int idx = base + tid, i = idx / P, part = idx % P;
+    int rank = 0;
+    int t = 0, e = 0;
+    if (i < n) {
+      t = i / E;
+      e = i - t * E;
+      const uint32_t kv = s_key[i];
+      const uint32_t* row = s_key + t * E;
+      const int f0 = part * chunk, f1 = min(E, f0 + chunk);
+      int f = f0;
+      if (((t * E + f0) & 3) == 0) {
+        for (; f + 16 <= f1; f += 16) {
+          uint4 o[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[u] = *reinterpret_cast<const uint4*>(row + f + 4 * u);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            rank += ranks_before(o[u].x, f + 4 * u, kv, e) +
+                    ranks_before(o[u].y, f + 4 * u + 1, kv, e) +
+                    ranks_before(o[u].z, f + 4 * u + 2, kv, e) +
+                    ranks_before(o[u].w, f + 4 * u + 3, kv, e);
+        }
+      }
+      for (; f < f1; ++f) rank += ranks_before(row[f], f, kv, e);
+    }
+    for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
+    if (i < n && part == 0 && rank < k) {
+      s_row[t * k + rank] = e;
+      s_selv[t * k + rank] = key_value(s_key[i]);
     }
   }
   __syncthreads();
-  const int rows = T * k;
+  // 2a. weights: softmax over each token's k selected logits (wave t)
+  if (wave < T) {
+    const int t = wave;
+    const float top = s_selv[t * k];
+    const float ex = lane < k ? expf(s_selv[t * k + lane] - top) : 0.f;
+    const float den = wave_sum(ex);
+    if (lane < k) {
+      ids[t * k + lane] = s_row[t * k + lane];
+      wts[t * k + lane] = ex / den;
+    }
+  }
+  // 2b. rows (wave 0): rank among the rows of the same expert, permuted
+  //     position and slot, from ballots over the expert-id bits
   if (wave == 0) {
     const bool act = lane < rows;
-    const int e = act ? s_ids[lane] : 0;
+    const int id = act ? s_row[lane] : 0;
     const uint64_t active = __ballot(act);
-    const uint64_t peers = match_peers(e, expert_bits(E), active);
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t eq = active, less = 0;  // rows with the same id / a smaller id
+    for (int b = expert_bits(E) - 1; b >= 0; --b) {
+      const int bit = (id >> b) & 1;
+      const uint64_t m1 = __ballot(act && bit);
+      if (bit) {
+        less |= eq & ~m1;
+        eq &= m1;
+      } else {
+        eq &= ~m1;
+      }
+    }
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int rk = __popcll(eq & below);
+    const uint64_t first = __ballot(act && rk == 0);
+    const int off = __popcll(less), slot = __popcll(less & first);
+    const int n_active = __popcll(first);
     if (act) {
-      s_rank[lane] = __popcll(peers & lt);
-      if ((peers & lt) == 0) s_cnt[e] = __popcll(peers);  // group leader
+      const int pos = off + rk;
+      perm_tok[pos] = lane / k;
+      inv_row[lane] = pos;
+      int32_t* rec = slots + kSlotRec * (1 + slot);
+      rec[kSlotTok + rk] = lane / k;
+      if (rk == 0) {
+        rec[0] = id;
+        rec[1] = off;
+        rec[2] = __popcll(eq);
+      }
+    }
+    if (n_shared && lane < T) {  // shared slot: rows T*k + t, token t
+      int32_t* rec = slots + kSlotRec * (1 + n_active);
+      if (lane == 0) {
+        rec[0] = -1;
+        rec[1] = rows;
+        rec[2] = T;
+      }
+      rec[kSlotTok + lane] = lane;
+    }
+    if (lane == 0) {
+      slots[0] = n_active + (n_shared ? 1 : 0);
+      offsets[E] = rows;
+      s_nact = n_active;
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    s_off[e] = s_cnt[e];
-    s_flag[e] = s_cnt[e] > 0;
+  // 3. every expert's count and offset, the row ids in registers
+  int rid[kDecodeMaxRoutedRows];
+#pragma unroll
+  for (int q4 = 0; q4 < kDecodeMaxRoutedRows / 4; ++q4) {
+    const int4 v = *reinterpret_cast<const int4*>(s_row + 4 * q4);
+    rid[4 * q4] = 4 * q4 < rows ? v.x : 0x7FFFFFFF;
+    rid[4 * q4 + 1] = 4 * q4 + 1 < rows ? v.y : 0x7FFFFFFF;
+    rid[4 * q4 + 2] = 4 * q4 + 2 < rows ? v.z : 0x7FFFFFFF;
+    rid[4 * q4 + 3] = 4 * q4 + 3 < rows ? v.w : 0x7FFFFFFF;
   }
-  __syncthreads();
-  const int total = block_exclusive_scan(s_off, E, s_tot);
-  const int n_active = block_exclusive_scan(s_flag, E, s_tot);
-  for (int e = tid; e < E; e += blockDim.x) {
-    counts[e] = s_cnt[e];
-    offsets[e] = s_off[e];
-    if (s_cnt[e] > 0) {
-      int32_t* rec = slots + kSlotRec * (1 + s_flag[e]);
-      rec[0] = e;
-      rec[1] = s_off[e];
-      rec[2] = s_cnt[e];
+  for (int e = tid; e < E; e += kSelThreads) {
+    int cnt = 0, off = 0;
+#pragma unroll
+    for (int r = 0; r < kDecodeMaxRoutedRows; ++r) {
+      cnt += rid[r] == e;
+      off += rid[r] < e;
     }
+    counts[e] = cnt;
+    offsets[e] = off;
   }
-  if (tid == 0) {
-    offsets[E] = total;
-    slots[0] = n_active + (n_shared ? 1 : 0);
-  }
-  if (n_shared && tid < T) {  // shared slot: rows T*k + t, token t
-    int32_t* rec = slots + kSlotRec * (1 + n_active);
-    if (tid == 0) {
-      rec[0] = -1;
-      rec[1] = rows;
-      rec[2] = T;
-    }
-    rec[kSlotTok + tid] = tid;
-  }
-  if (tid < rows) {
-    const int e = s_ids[tid];
-    const int pos = s_off[e] + s_rank[tid];
-    perm_tok[pos] = tid / k;
-    inv_row[tid] = pos;
-    slots[kSlotRec * (1 + s_flag[e]) + kSlotTok + s_rank[tid]] = tid / k;
+  // records past the last slot: no rows (a decode block reads only its own
+  // record and stops on M == 0)
+  const int n_slots = s_nact + (n_shared ? 1 : 0);
+  for (int sidx = n_slots + tid; sidx < max_slots; sidx += kSelThreads) {
+    int32_t* rec = slots + kSlotRec * (1 + sidx);
+    rec[0] = 0;
+    rec[1] = 0;
+    rec[2] = 0;
   }
 }
 
@@ -442,15 +600,17 @@ int launch_decode_route(const moe_layer* L, const uint16_t* x, int T, uint32_t f
   const int E = L->n_experts, k = L->top_k, d = L->d;
   const int do_logits = !(flags & MOE_LOGITS_GIVEN);
   if (mask & MOE_DECODE_STAGE_ROUTE) {
-    dim3 grid(max((E + 3) / 4, 64), 1);
-    hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
+    const int G = d / 32;
+    dim3 grid(max(E, (T * G + 7) / 8));
+    hipLaunchKernelGGL(k_dec_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
                        L->router_bias, R->logits, do_logits, (uint16_t*)(ws + W.xs),
                        (uint16_t*)(ws + W.xsum));
   }
   if (mask & MOE_DECODE_STAGE_SELECT)
-    hipLaunchKernelGGL(k_dec_select, dim3(1), dim3(512), 0, s, R->logits, T, E, k, L->n_shared,
+    hipLaunchKernelGGL(k_dec_select, dim3(1), dim3(kSelThreads), 0, s, R->logits, T, E, k,
+                       L->n_shared,
                        R->topk_ids, R->topk_w, R->counts, R->offsets, R->perm_tok, R->inv_row,
-                       (int32_t*)(ws + W.slots));
+                       (int32_t*)(ws + W.slots), W.max_slots);
   return (int)hipGetLastError();
 }
 

@@ -41,7 +41,8 @@ def _functions(text, prefix):
 
 def test_tile_loads_match_the_copy_wait(asm):
     funcs = _functions(asm, "_ZN5bqmoe10k_dec_proj")
-    assert len(funcs) >= 20
+    funcs.update(_functions(asm, "_ZN5bqmoe18k_dec_down_combine"))
+    assert len(funcs) >= 30
     for name, body in funcs.items():
         lines = [l.strip() for l in body.splitlines()]
         lds = [i for i, l in enumerate(lines) if l.startswith("global_load_lds")]
