@@ -72,7 +72,13 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--kernel-loop", type=int, default=0,
-                    help="profiling aid: only launch the decode gate/up stage this many times")
+                    help="profiling aid: only launch one decode stage (--loop-stage) this many "
+                         "times")
+    ap.add_argument("--loop-stage", default="gateup", choices=["gateup", "down"],
+                    help="the stage --kernel-loop launches")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="profiling aid: only run 10 device copies of 256 MiB (a plain copy of "
+                         "known size, to calibrate the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -150,9 +156,10 @@ def decode_leg(args, dev):
     torch.cuda.synchronize()
     GU = bq.MOE_DECODE_STAGE_GATEUP
     if args.kernel_loop:
+        st = GU if args.loop_stage == "gateup" else bq.MOE_DECODE_STAGE_DOWN
         for r in range(args.kernel_loop):
             j = r % C
-            bq.moe_forward_decode_stages(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j], GU)
+            bq.moe_forward_decode_stages(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j], st)
         torch.cuda.synchronize()
         return None
     reps = max(K, 8 * C)
@@ -305,6 +312,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = "cuda:0"
+    if args.traffic_probe:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe_bytes_per_copy": n, "copies": 10}), flush=True)
+        return
     import bit_quantized_moe_router_amd as bq
 
     bq.load()
