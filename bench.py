@@ -76,6 +76,8 @@ def parse():
                          "times")
     ap.add_argument("--loop-stage", default="gateup", choices=["gateup", "down"],
                     help="the stage --kernel-loop launches")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="profiling aid: run only the prefill leg and print its result")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="profiling aid: only run 10 device copies of 256 MiB (a plain copy of "
                          "known size, to calibrate the HBM byte counters)")
@@ -324,6 +326,9 @@ def main():
     import bit_quantized_moe_router_amd as bq
 
     bq.load()
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_leg(args, dev)}), flush=True)
+        return
     d = decode_leg(args, dev)
     if d is None:  # profiling loop only
         return

@@ -42,37 +42,6 @@ constexpr int kDecMaxRows = 8;  // rows of one slot (<= T <= 8)
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-// Masks and bases of the 2-bit unpacking (see unpack2 in device_common.h),
-// passed as kernel arguments.  The masks stay in scalar registers and the
-// bases are copied once into vector registers (an identity lane move), so
-// that each mask-and-or is one v_and_or_b32: with literal constants, or with
-// both operands scalar, it would take two instructions (a VOP3 op here takes
-// no literal and at most one scalar operand).
-struct Unpack2K {
-  uint32_t m0, m1, m2, b0, b1, b2;
-};
-static const Unpack2K kUnpack2 = {0x00030003u, 0x000C000Cu, 0x00300030u,
-                                  0x45004500u, 0x44004400u, 0x43004300u};
-
-__device__ __forceinline__ uint32_t lane_copy(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, true);  // quad_perm 0,1,2,3
-}
-
-struct Unpack2R {
-  uint32_t m0, m1, m2, b0, b1, b2;  // b* in vector registers
-};
-
-template <int P>
-__device__ __forceinline__ u32x4 unpack2_r(uint32_t w, const Unpack2R& c) {
-  const uint32_t x = P ? (w >> 8) : w;
-  u32x4 r;
-  r[0] = (x & c.m0) | c.b0;
-  r[1] = (x & c.m1) | c.b1;
-  r[2] = (x & c.m2) | c.b2;
-  r[3] = ((x >> 2) & c.m2) | c.b2;
-  return r;
-}
-
 // LDS region of one wave: activation rows [M][KBW*128 bf16 + 16 B pad], then
 // staged sums [M][KBW*4][16 B]; each part rounded up to whole KB, as the
 // direct loads fill 1 KB per instruction.
@@ -132,41 +101,39 @@ __device__ __forceinline__ void dec_stage_rows(uint8_t* sA, uint8_t* sS, int lan
   }
 }
 
-// 2. Packed tiles of a wave's k-blocks for NS streams: codes (8 B / lane),
-//    level bit 2 (4 B / lane, 3-bit only), scales of row r, groups q & 2 and
-//    (q & 2) + 1 (4 B / lane).  Stream j reads n-tile nt[j] of projection
-//    second(j) = (GATEUP && j == 1).  The loads are unconditional (a wave past
-//    the last k-block re-reads the last tile) so that their number is the
-//    compile-time constant dec_tile_loads().
+// 2. Packed tiles of one of a wave's k-blocks (kb0 + i) for NS streams: codes
+//    (8 B / lane), level bit 2 (4 B / lane, 3-bit only), scales of row r,
+//    groups q & 2 and (q & 2) + 1 (4 B / lane).  Stream j reads n-tile nt[j]
+//    of projection second(j) = (GATEUP && j == 1).  The loads are
+//    unconditional (a wave past the last k-block re-reads the last tile), so
+//    that their number per k-block is the compile-time constant
+//    dec_kb_loads().
 template <int NS, bool GATEUP, bool QA3, bool QB3>
-__host__ __device__ constexpr int dec_tile_loads(int kbw) {
-  return kbw * ((2 + (QA3 ? 1 : 0)) + (NS - 1) * (2 + ((GATEUP ? QB3 : QA3) ? 1 : 0)));
+__host__ __device__ constexpr int dec_kb_loads() {
+  return (2 + (QA3 ? 1 : 0)) + (NS - 1) * (2 + ((GATEUP ? QB3 : QA3) ? 1 : 0));
 }
 
 template <int NS, bool GATEUP, bool QA3, bool QB3, int KBW>
-__device__ __forceinline__ void dec_load_tiles(u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS],
-                                               uint32_t (&ws)[KBW][NS],
-                                               const uint8_t* const (&code_base)[2],
-                                               const size_t (&plane1)[2],
-                                               const size_t (&scale_off)[2],
-                                               const int (&nt)[NS], int KB, int kb0, int lane) {
+__device__ __forceinline__ void dec_load_kb(int i, u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS],
+                                            uint32_t (&ws)[KBW][NS],
+                                            const uint8_t* const (&code_base)[2],
+                                            const size_t (&plane1)[2],
+                                            const size_t (&scale_off)[2], const int (&nt)[NS],
+                                            int KB, int kb0, int lane) {
   const int q = lane >> 4, r = lane & 15;
+  const int kbc = min(kb0 + i, KB - 1);
 #pragma unroll
-  for (int i = 0; i < KBW; ++i) {
-    const int kbc = min(kb0 + i, KB - 1);
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int second = GATEUP && j == 1;
-      const bool q3 = second ? QB3 : QA3;
-      const uint8_t* base = code_base[second];
-      const size_t tile = (size_t)nt[j] * KB + kbc;
-      wc[i][j] = *reinterpret_cast<const u32x2*>(base + tile * 512 + lane * 8);
-      wh[i][j] = q3 ? *reinterpret_cast<const uint32_t*>(base + plane1[second] + tile * 256 +
-                                                         lane * 4)
-                    : 0u;
-      ws[i][j] = *reinterpret_cast<const uint32_t*>(base + scale_off[second] + tile * 128 +
-                                                    (r * 4 + (q & 2)) * 2);
-    }
+  for (int j = 0; j < NS; ++j) {
+    const int second = GATEUP && j == 1;
+    const bool q3 = second ? QB3 : QA3;
+    const uint8_t* base = code_base[second];
+    const size_t tile = (size_t)nt[j] * KB + kbc;
+    wc[i][j] = *reinterpret_cast<const u32x2*>(base + tile * 512 + lane * 8);
+    wh[i][j] =
+        q3 ? *reinterpret_cast<const uint32_t*>(base + plane1[second] + tile * 256 + lane * 4)
+           : 0u;
+    ws[i][j] = *reinterpret_cast<const uint32_t*>(base + scale_off[second] + tile * 128 +
+                                                  (r * 4 + (q & 2)) * 2);
   }
 }
 
@@ -197,51 +164,80 @@ __device__ __forceinline__ void dec_half_sums_to_staged(uint8_t* sS, int lane, i
   }
 }
 
-// 4. Matrix-core work over a wave's k-blocks; per 32-group one correction op
-//    (two if the projections differ) and one op per stream; the group's scale
+// 4. Matrix-core work on one k-block; per 32-group one correction op (two if
+//    the projections differ) and one op per stream; the group's scale
 //    multiplies MR accumulator rows (rows 4*(lane/16) + i carry real rows for
 //    i < M; MR = 1 when M == 1).
 template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int MR>
-__device__ __forceinline__ void dec_mfma(f32x4 (&acc)[NS], const u32x2 (&wc)[KBW][NS],
-                                         const uint32_t (&wh)[KBW][NS],
-                                         const uint32_t (&ws)[KBW][NS], int nkb,
-                                         const uint8_t* aptr, const uint8_t* sptr, u32x4 bca,
-                                         u32x4 bcb, const Unpack2R& ur, int r) {
+__device__ __forceinline__ void dec_mfma_kb(int i, f32x4 (&acc)[NS], const u32x2 (&wc)[KBW][NS],
+                                            const uint32_t (&wh)[KBW][NS],
+                                            const uint32_t (&ws)[KBW][NS], const uint8_t* aptr,
+                                            const uint8_t* sptr, u32x4 bca, u32x4 bcb,
+                                            const Unpack2R& ur, int r) {
 #pragma unroll
-  for (int i = 0; i < KBW; ++i) {
-    if (i < nkb) {
+  for (int GB = 0; GB < 4; ++GB) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(aptr + (i * 128 + GB * 32) * 2);
+    const u32x4 sv = *reinterpret_cast<const u32x4*>(sptr + (i * 4 + GB) * 16);
+    const f32x4 corr_a = mfma_corr(sv, bca);
+    f32x4 corr_b = corr_a;
+    if constexpr (!SAMEC) corr_b = mfma_corr(sv, bcb);
 #pragma unroll
-      for (int GB = 0; GB < 4; ++GB) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(aptr + (i * 128 + GB * 32) * 2);
-        const u32x4 sv = *reinterpret_cast<const u32x4*>(sptr + (i * 4 + GB) * 16);
-        const f32x4 corr_a = mfma_corr(sv, bca);
-        f32x4 corr_b = corr_a;
-        if constexpr (!SAMEC) corr_b = mfma_corr(sv, bcb);
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          const bool second = GATEUP && j == 1;
-          const bool q3 = second ? QB3 : QA3;
-          const uint32_t word = (GB < 2) ? wc[i][j][0] : wc[i][j][1];
-          u32x4 b;
-          if (q3) {
-            if (GB == 0) b = unpack3<0>(word, wh[i][j]);
-            if (GB == 1) b = unpack3<1>(word, wh[i][j]);
-            if (GB == 2) b = unpack3<2>(word, wh[i][j]);
-            if (GB == 3) b = unpack3<3>(word, wh[i][j]);
-          } else {
-            b = (GB & 1) ? unpack2_r<1>(word, ur) : unpack2_r<0>(word, ur);
-          }
-          const f32x4 dd = mfma32(a, b, second ? corr_b : corr_a);
-          // lane GB*16 + r holds scales (r, GB & 2) and (r, (GB & 2) + 1)
-          const uint32_t sw = (uint32_t)__shfl((int)ws[i][j], GB * 16 + r, 64);
-          const float s = f16_to_f32((GB & 1) ? (sw >> 16) : sw);
-#pragma unroll
-          for (int m = 0; m < MR; ++m) acc[j][m] = fmaf(s, dd[m], acc[j][m]);
-        }
+    for (int j = 0; j < NS; ++j) {
+      const bool second = GATEUP && j == 1;
+      const bool q3 = second ? QB3 : QA3;
+      const uint32_t word = (GB < 2) ? wc[i][j][0] : wc[i][j][1];
+      u32x4 b;
+      if (q3) {
+        if (GB == 0) b = unpack3<0>(word, wh[i][j]);
+        if (GB == 1) b = unpack3<1>(word, wh[i][j]);
+        if (GB == 2) b = unpack3<2>(word, wh[i][j]);
+        if (GB == 3) b = unpack3<3>(word, wh[i][j]);
+      } else {
+        b = (GB & 1) ? unpack2_r<1>(word, ur) : unpack2_r<0>(word, ur);
       }
+      const f32x4 dd = mfma32(a, b, second ? corr_b : corr_a);
+      // lane GB*16 + r holds scales (r, GB & 2) and (r, (GB & 2) + 1)
+      const uint32_t sw = (uint32_t)__shfl((int)ws[i][j], GB * 16 + r, 64);
+      const float s = f16_to_f32((GB & 1) ? (sw >> 16) : sw);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) acc[j][m] = fmaf(s, dd[m], acc[j][m]);
     }
   }
 }
+
+// Tile loads run PRE k-blocks ahead of the matrix-core work, in the wave's
+// own instruction stream: when the memory system pushes back on issue, the
+// wave keeps computing on the tiles it already has.  On entry the loads of
+// k-blocks 0 .. PRE-1 are issued and the copies into LDS have landed.
+template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, int MR>
+__device__ __forceinline__ void dec_pipeline(f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS],
+                                             uint32_t (&wh)[KBW][NS], uint32_t (&ws)[KBW][NS],
+                                             const uint8_t* const (&code_base)[2],
+                                             const size_t (&plane1)[2],
+                                             const size_t (&scale_off)[2], const int (&nt)[NS],
+                                             int KB, int kb0, int nkb, int lane,
+                                             const uint8_t* aptr, const uint8_t* sptr, u32x4 bca,
+                                             u32x4 bcb, const Unpack2R& ur) {
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    if (i + PRE < KBW) {
+      dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i + PRE, wc, wh, ws, code_base, plane1, scale_off,
+                                             nt, KB, kb0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < nkb)
+      dec_mfma_kb<NS, GATEUP, QA3, QB3, SAMEC, KBW, MR>(i, acc, wc, wh, ws, aptr, sptr, bca, bcb,
+                                                        ur, lane & 15);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// k-blocks whose tile loads run ahead of the matrix-core work.  Shallow on
+// purpose: every wave of the launch streams at once, the memory pipeline is
+// saturated throughout, and deeper per-wave prefetch only lets the oldest waves
+// hold the issue queue longer (measured: 1 ahead is best for 8 k-blocks per
+// wave, 2 for 16).
+__host__ __device__ constexpr int dec_pre(int kbw) { return kbw >= 16 ? 2 : 1; }
 
 // ------------------------------------------------------- projection kernel
 // GATEUP = true: streams 0 (gate) and 1 (up) of n-tile blockIdx % groups;
@@ -291,11 +287,14 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
   int nt[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) nt[j] = GATEUP ? grp : grp * 4 + j;
+  constexpr int PRE = dec_pre(KBW);
   u32x2 wc[KBW][NS];
   uint32_t wh[KBW][NS], ws[KBW][NS];
-  dec_load_tiles<NS, GATEUP, QA3, QB3, KBW>(wc, wh, ws, code_base, plane1, scale_off, nt, KB,
-                                            kb0, lane);
-  wait_for_copies<dec_tile_loads<NS, GATEUP, QA3, QB3>(KBW)>();
+#pragma unroll
+  for (int i = 0; i < PRE; ++i)
+    dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
+                                           kb0, lane);
+  wait_for_copies<PRE * dec_kb_loads<NS, GATEUP, QA3, QB3>()>();
   if constexpr (!GATEUP) dec_half_sums_to_staged<KBW>(sS, lane, M, nkb);
 
   const u32x4 bca = corr_b_operand(q == 0, QA3, ca);
@@ -308,11 +307,13 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (ONE_ROW || M == 1)
-    dec_mfma<NS, GATEUP, QA3, QB3, SAMEC, KBW, 1>(acc, wc, wh, ws, nkb, aptr, sptr, bca, bcb, ur,
-                                                  r);
+    dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 1>(acc, wc, wh, ws, code_base, plane1,
+                                                           scale_off, nt, KB, kb0, nkb, lane,
+                                                           aptr, sptr, bca, bcb, ur);
   else
-    dec_mfma<NS, GATEUP, QA3, QB3, SAMEC, KBW, 4>(acc, wc, wh, ws, nkb, aptr, sptr, bca, bcb, ur,
-                                                  r);
+    dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 4>(acc, wc, wh, ws, code_base, plane1,
+                                                           scale_off, nt, KB, kb0, nkb, lane,
+                                                           aptr, sptr, bca, bcb, ur);
 
   // 5. cross-wave reduction in a fixed order (every wave is done with LDS)
   __syncthreads();
@@ -407,11 +408,14 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
     dec_stage_rows<KBW>(sA, sS, lane, M, false, row0, 0u, hs, hsum, K, 0, KB);
     __builtin_amdgcn_sched_barrier(0);
     const int ntl[1] = {nt};
+    constexpr int PRE = dec_pre(KBW);
     u32x2 wc[KBW][1];
     uint32_t wh[KBW][1], ws[KBW][1];
-    dec_load_tiles<1, false, Q3, Q3, KBW>(wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0,
-                                          lane);
-    wait_for_copies<dec_tile_loads<1, false, Q3, Q3>(KBW)>();
+#pragma unroll
+    for (int i = 0; i < PRE; ++i)
+      dec_load_kb<1, false, Q3, Q3, KBW>(i, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0,
+                                         lane);
+    wait_for_copies<PRE * dec_kb_loads<1, false, Q3, Q3>()>();
     dec_half_sums_to_staged<KBW>(sS, lane, M, KB);
     const u32x4 bc = corr_b_operand(q == 0, Q3, cd);
     const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1),
@@ -421,9 +425,13 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
     const uint8_t* sptr = sS + arow * KBW * 64;
     f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
     if (ONE_ROW || M == 1)
-      dec_mfma<1, false, Q3, Q3, true, KBW, 1>(acc, wc, wh, ws, KB, aptr, sptr, bc, bc, ur, r);
+      dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 1>(acc, wc, wh, ws, code_base, plane1,
+                                                        scale_off, ntl, KB, 0, KB, lane, aptr,
+                                                        sptr, bc, bc, ur);
     else
-      dec_mfma<1, false, Q3, Q3, true, KBW, 4>(acc, wc, wh, ws, KB, aptr, sptr, bc, bc, ur, r);
+      dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 4>(acc, wc, wh, ws, code_base, plane1,
+                                                        scale_off, ntl, KB, 0, KB, lane, aptr,
+                                                        sptr, bc, bc, ur);
     // rows 4*(lane/16) + i, column lane % 16 -> y of permuted row row0 + row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

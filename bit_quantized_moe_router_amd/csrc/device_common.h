@@ -153,4 +153,35 @@ __device__ __forceinline__ uint32_t level_bf16(uint32_t u, float off) {
   return f32_to_bf16((float)u - off);
 }
 
+// Masks and bases of the 2-bit unpacking (see unpack2 in device_common.h),
+// passed as kernel arguments.  The masks stay in scalar registers and the
+// bases are copied once into vector registers (an identity lane move), so
+// that each mask-and-or is one v_and_or_b32: with literal constants, or with
+// both operands scalar, it would take two instructions (a VOP3 op here takes
+// no literal and at most one scalar operand).
+struct Unpack2K {
+  uint32_t m0, m1, m2, b0, b1, b2;
+};
+static constexpr Unpack2K kUnpack2 = {0x00030003u, 0x000C000Cu, 0x00300030u,
+                                  0x45004500u, 0x44004400u, 0x43004300u};
+
+__device__ __forceinline__ uint32_t lane_copy(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, true);  // quad_perm 0,1,2,3
+}
+
+struct Unpack2R {
+  uint32_t m0, m1, m2, b0, b1, b2;  // b* in vector registers
+};
+
+template <int P>
+__device__ __forceinline__ u32x4 unpack2_r(uint32_t w, const Unpack2R& c) {
+  const uint32_t x = P ? (w >> 8) : w;
+  u32x4 r;
+  r[0] = (x & c.m0) | c.b0;
+  r[1] = (x & c.m1) | c.b1;
+  r[2] = (x & c.m2) | c.b2;
+  r[3] = ((x >> 2) & c.m2) | c.b2;
+  return r;
+}
+
 }  // namespace bqmoe

@@ -65,14 +65,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 // LDS per buffer: 16 chunk columns x kRows rows x 16 B of activations (chunk c
 // of row R at c*kRows*16 + R*16: the 16 rows a matrix-core read touches are 256
 // contiguous bytes, and every address is one base register plus an immediate),
-// then kRows rows x 64 B of group sums (4 groups x 16 B).  Both are filled
+// then the group sums in the same column form (group g of row R at
+// g*kRows*16 + R*16).  Both are filled
 // with direct global->LDS loads (64 lanes x 16 B = 64 rows of one chunk column
 // per instruction), which need no registers.
 constexpr int kColBytes = kRows * 16;
 constexpr int kBufBytes = kRows * 256 + kRows * 64;
 constexpr int kDmaA = 16 * kRows / 64;   // activation DMA instructions per k-block
-constexpr int kDmaS = kRows * 64 / 1024; // group-sum DMA instructions per k-block
-static_assert(kRows % 64 == 0 && kDmaA % 4 == 0 && kDmaS <= 4, "tile rows");
+constexpr int kDmaS = 4;                  // group-sum DMA instructions per k-block (one per group)
+static_assert(kRows == 64 && kDmaA % 4 == 0, "one row per lane in the group-sum loads");
 
 template <int NMAT, int NTPW, bool Q3A, bool Q3B, bool SAMEC>
 __global__ __launch_bounds__(256, 2) void k_pf_gemm(
@@ -80,13 +81,22 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ tiles, const int32_t* __restrict__ ctrl,
     const int32_t* __restrict__ perm_tok, int Tk, int gather, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Asum, int K, int N, float ca, float cb,
-    uint16_t* __restrict__ out, uint16_t* __restrict__ out_sum) {
+    uint16_t* __restrict__ out, uint16_t* __restrict__ out_sum, int ncol, Unpack2K uk) {
   static_assert(NMAT * NTPW == 4, "four (projection, n-tile) streams per wave");
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * kBufBytes];
   __shared__ int sTok[kRows];
 
-  if ((int)blockIdx.x >= ctrl[0]) return;
-  const int32_t* tl = tiles + 4 * blockIdx.x;
+  // Work item = (row tile, column group), tile-major.  Blocks go to the 8 XCDs
+  // round-robin; each XCD takes one contiguous chunk of the items, so the
+  // column groups of a row tile run together on one XCD and read the tile's
+  // activations from that XCD's L2 instead of from HBM once per column group.
+  const int n_items = ctrl[0] * ncol;
+  const int chunk = (n_items + 7) / 8;
+  const int local = blockIdx.x / 8;
+  const int item = (blockIdx.x % 8) * chunk + local;
+  if (local >= chunk || item >= n_items) return;
+  const int tile = item / ncol, col = item % ncol;
+  const int32_t* tl = tiles + 4 * tile;
   const int e = tl[0], row0 = tl[1], M = tl[2];
   const uint8_t* blob = e >= 0 ? experts + (size_t)e * stride : shared;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
@@ -104,15 +114,18 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
   const uint16_t* arow[kRows / 64];
 #pragma unroll
   for (int h = 0; h < kRows / 64; ++h) arow[h] = A + (size_t)sTok[64 * h + lane] * K;
-  // group sums: instruction i covers rows 16*i .. 16*i+15, 4 lanes (groups) per row
-  const int s_wave_row = (wave < kDmaS ? wave : 0) * 16 + (lane >> 2);
-  const uint16_t* srow = Asum + ((size_t)sTok[s_wave_row] * G + (lane & 3)) * 8;
+  // group sums, stored group-major in LDS ([group][row][16 B]: the 16 rows a
+  // matrix-core read touches are contiguous, free of bank conflicts); wave w
+  // loads group w of the k-block, one row per lane
+  const uint16_t* srow = Asum + ((size_t)sTok[lane] * G + (wave & 3)) * 8;
 
   // this wave's streams: stream j -> projection (j / NTPW), n-tile nt0 + j % NTPW
-  const int nt0 = (blockIdx.y * 4 + wave) * NTPW;
+  const int nt0 = (col * 4 + wave) * NTPW;
   const uint8_t* const base0 = blob + pa.off;
   const uint8_t* const base1 = blob + pb.off;
+  const size_t scl0 = pa.scales, scl1 = pb.scales, pl0 = pa.plane1, pl1 = pb.plane1;
 
+  const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1), lane_copy(uk.b2)};
   const u32x4 bc0 = corr_b_operand(q == 0, Q3A, ca);
   const u32x4 bc1 = corr_b_operand(q == 0, Q3B, cb);
 
@@ -122,8 +135,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x2 pw[4], ps[4];
-  uint32_t ph[4];
+  // packed tiles of the k-block being used (c*) and of the next one, in flight (n*)
+  u32x2 cw[4], cs[4], nw[4], ns[4];
+  uint32_t ch[4], nh[4];
 
 #define BQ_ISSUE(KB_, BUF_)                                                                    \
   {                                                                                            \
@@ -141,60 +155,73 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
                                        (lds_void*)(dst + kRows * 256 + wave * 1024), 16, 0, 0); \
   }
 
-#define BQ_LOADB(KB_)                                                                          \
+#define BQ_LOADB(KB_, S_)                                                                      \
   {                                                                                            \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                            \
       const bool first = (j / NTPW == 0);                                                      \
       const uint8_t* bb = first ? base0 : base1;                                               \
-      const ProjDesc& pp = first ? pa : pb;                                                    \
       const size_t tile = (size_t)(nt0 + (j % NTPW)) * KB + (KB_);                             \
-      pw[j] = *reinterpret_cast<const u32x2*>(bb + tile * 512 + lane * 8);                     \
-      ps[j] = *reinterpret_cast<const u32x2*>(bb + pp.scales + tile * 128 + r * 8);            \
+      S_##w[j] = *reinterpret_cast<const u32x2*>(bb + tile * 512 + lane * 8);                  \
+      S_##s[j] = *reinterpret_cast<const u32x2*>(bb + (first ? scl0 : scl1) + tile * 128 +     \
+                                                 r * 8);                                       \
       const bool q3 = first ? Q3A : Q3B;                                                       \
-      ph[j] = q3 ? *reinterpret_cast<const uint32_t*>(bb + pp.plane1 + tile * 256 + lane * 4)  \
-                 : 0u;                                                                         \
+      S_##h[j] = q3 ? *reinterpret_cast<const uint32_t*>(bb + (first ? pl0 : pl1) +            \
+                                                         tile * 256 + lane * 4)                \
+                    : 0u;                                                                      \
     }                                                                                          \
   }
 
+  // k-block kb: wait for its activations (LDS) and tiles (registers), then
+  // issue k-block kb+1 into the other buffer and register set, then compute
   BQ_ISSUE(0, 0)
+  BQ_LOADB(0, c)
   for (int kb = 0; kb < KB; ++kb) {
     const int buf = kb & 1;
-    BQ_LOADB(kb)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // k-block kb is in LDS for every wave; buffer buf^1 is free
-    const u32x2* cw = pw;
-    const u32x2* cs = ps;
-    const uint32_t* chh = ph;
-    if (kb + 1 < KB) BQ_ISSUE(kb + 1, buf ^ 1)
+    if (kb + 1 < KB) {
+      BQ_ISSUE(kb + 1, buf ^ 1)
+      BQ_LOADB(kb + 1, n)
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* sA = sbuf + buf * kBufBytes;
     const uint8_t* sS = sA + kRows * 256;
 
 #define BQ_PF_GROUP(GB)                                                                         \
   {                                                                                             \
+    /* the group's LDS reads first (all row tiles), so that their latency runs */              \
+    /* under the unpacking below rather than in front of each matrix-core op */                \
+    u32x4 av[RT], aa[RT];                                                                       \
+    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                         \
+      /* lanes q != 0 meet zeros in the correction B operand: no select needed */              \
+      av[rt] = *reinterpret_cast<const u32x4*>(sS + GB * kColBytes + (rt * 16 + r) * 16);       \
+      aa[rt] = *reinterpret_cast<const u32x4*>(sA + (GB * 4 + q) * kColBytes + (rt * 16 + r) * 16); \
+    }                                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
     u32x4 b[4];                                                                                 \
     float sc[4];                                                                                \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                             \
       const bool q3 = (j / NTPW == 0) ? Q3A : Q3B;                                              \
-      b[j] = q3 ? unpack_b<true, GB>(cw[j], chh[j]) : unpack_b<false, GB>(cw[j], chh[j]);       \
+      if (q3)                                                                                   \
+        b[j] = unpack_b<true, GB>(cw[j], ch[j]);                                                \
+      else                                                                                      \
+        b[j] = unpack2_r<GB & 1>((GB < 2) ? cw[j][0] : cw[j][1], ur);                           \
       const uint32_t sbits = ((GB < 2) ? cs[j][0] : cs[j][1]) >> (16 * (GB & 1));               \
       sc[j] = f16_to_f32(sbits & 0xFFFFu);                                                      \
+      /* an fp32 register: plain FMAs below rather than mixed-precision ones */                 \
+      asm volatile("" : "+v"(sc[j]));                                                           \
     }                                                                                           \
     _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                         \
-      const uint4 sv = *reinterpret_cast<const uint4*>(sS + (rt * 16 + r) * 64 + GB * 16);     \
-      const u32x4 av = {q == 0 ? sv.x : 0u, q == 0 ? sv.y : 0u, q == 0 ? sv.z : 0u, 0u};         \
-      const f32x4 corr0 = mfma_corr(av, bc0);                           \
+      const f32x4 corr0 = mfma_corr(av[rt], bc0);                                               \
       f32x4 corr1 = corr0;                                                                      \
-      if constexpr (!SAMEC) corr1 = mfma_corr(av, bc1);               \
-      const u32x4 a =                                                                           \
-          *reinterpret_cast<const u32x4*>(sA + (GB * 4 + q) * kColBytes + (rt * 16 + r) * 16);  \
+      if constexpr (!SAMEC) corr1 = mfma_corr(av[rt], bc1);                                     \
       _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                           \
-        const f32x4 dd = mfma32(a, b[j], (j / NTPW == 0) ? corr0 : corr1);                      \
+        const f32x4 dd = mfma32(aa[rt], b[j], (j / NTPW == 0) ? corr0 : corr1);                 \
         acc[rt][j][0] = fmaf(sc[j], dd[0], acc[rt][j][0]);                                      \
         acc[rt][j][1] = fmaf(sc[j], dd[1], acc[rt][j][1]);                                      \
         acc[rt][j][2] = fmaf(sc[j], dd[2], acc[rt][j][2]);                                      \
         acc[rt][j][3] = fmaf(sc[j], dd[3], acc[rt][j][3]);                                      \
       }                                                                                         \
-      __builtin_amdgcn_sched_barrier(0);                                                        \
     }                                                                                           \
   }
     BQ_PF_GROUP(0)
@@ -205,6 +232,13 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
     __builtin_amdgcn_sched_barrier(0);
     BQ_PF_GROUP(3)
 #undef BQ_PF_GROUP
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cw[j] = nw[j];
+      cs[j] = ns[j];
+      ch[j] = nh[j];
+    }
   }
 #undef BQ_ISSUE
 #undef BQ_LOADB
@@ -346,7 +380,7 @@ static void launch_gu(dim3 grid, hipStream_t s, const moe_layer* L, ProjDesc pg,
   hipLaunchKernelGGL((k_pf_gemm<2, 2, A3, B3, SAMEC>), grid, dim3(256), 0, s, (const uint8_t*)L->experts,
                      L->expert_stride, (const uint8_t*)L->shared, pg, pu, tiles, ctrl, perm_tok, Tk,
                      1, xs, xsum, L->d, L->inter, qtype_offset(L->q_gate), qtype_offset(L->q_up), hs,
-                     hsum);
+                     hsum, L->inter / 128, kUnpack2);
 }
 
 int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
@@ -371,7 +405,8 @@ int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
     hipLaunchKernelGGL(k_stage, dim3(blocks), dim3(256), 0, s, x, T, d, xs, xsum);
   }
   const ProjDesc pg = proj_pf(L, 0), pu = proj_pf(L, 1), pdn = proj_pf(L, 2);
-  dim3 g1(P.max_tiles, I / 128);
+  // grids: every (row tile, column group) item of the largest possible tile list
+  const dim3 g1((unsigned)(((long)P.max_tiles * (I / 128) + 7) / 8 * 8));
   if (mask & MOE_PREFILL_STAGE_GATEUP) {
   const bool g3 = L->q_gate == MOE_Q_INT3, u3 = L->q_up == MOE_Q_INT3;
   const bool same = L->q_gate == L->q_up;  // same correction operand
@@ -386,18 +421,18 @@ int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
   else
     launch_gu<false, false, false>(g1, s, L, pg, pu, tiles, ctrl, R->perm_tok, Tk, xs, xsum, hs, hsum);
   }
-  dim3 g2(P.max_tiles, d / 256);
+  const dim3 g2((unsigned)(((long)P.max_tiles * (d / 256) + 7) / 8 * 8));
   if (!(mask & MOE_PREFILL_STAGE_DOWN)) {
   } else if (L->q_down == MOE_Q_INT3)
     hipLaunchKernelGGL((k_pf_gemm<1, 4, true, true, true>), g2, dim3(256), 0, s,
                        (const uint8_t*)L->experts, L->expert_stride, (const uint8_t*)L->shared, pdn,
                        pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hsum, I, d, qtype_offset(L->q_down),
-                       qtype_offset(L->q_down), y, (uint16_t*)nullptr);
+                       qtype_offset(L->q_down), y, (uint16_t*)nullptr, d / 256, kUnpack2);
   else
     hipLaunchKernelGGL((k_pf_gemm<1, 4, false, false, true>), g2, dim3(256), 0, s,
                        (const uint8_t*)L->experts, L->expert_stride, (const uint8_t*)L->shared, pdn,
                        pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hsum, I, d, qtype_offset(L->q_down),
-                       qtype_offset(L->q_down), y, (uint16_t*)nullptr);
+                       qtype_offset(L->q_down), y, (uint16_t*)nullptr, d / 256, kUnpack2);
   if (mask & MOE_PREFILL_STAGE_COMBINE) {
     const int rc = launch_combine(y, T, d, k, L->n_shared, R->inv_row, R->topk_w, x,
                                   (flags & MOE_ADD_RESIDUAL) ? 1 : 0, out, stream);
