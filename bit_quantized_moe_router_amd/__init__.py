@@ -69,6 +69,9 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it first (python -c "
                           "'import __graft_entry__ as g; g.build()').  There is no CPU fallback.")
+    if torch.cuda.is_available():
+        # bring the HIP runtime up before the library registers its code objects
+        torch.cuda.init()
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32, i64, u32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64,
                              ctypes.c_uint32)

@@ -79,47 +79,48 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   }
 }
 
-// Decode router logits (T <= 8): block per expert, its 4 waves split d and
-// issue all of their router-row loads at once (the row is read once for all
-// T tokens); partial sums meet in LDS.  The blocks also stage x for the
-// expert kernels: xs = x/16 (exact) and, per 32-group, the staged sums.
+// Decode router logits (TT = T <= 8 tokens, a compile-time count so that
+// every load of a step is unconditional and all of them are in flight
+// together): block per expert, its 4 waves split d; the router row is read
+// once for all T tokens and the partial sums meet in LDS.  The blocks also
+// stage x for the expert kernels: xs = x/16 (exact) and, per 32-group, the
+// staged sums.
+template <int TT>
 __global__ __launch_bounds__(256) void k_dec_logits(const uint16_t* __restrict__ x, int T, int d,
                                                     int E, const float* __restrict__ Wr,
                                                     const float* __restrict__ bias,
                                                     float* __restrict__ logits, int do_logits,
                                                     uint16_t* __restrict__ xs,
                                                     uint16_t* __restrict__ xsum) {
-  __shared__ float s_part[4][MOE_MAX_DECODE_TOKENS];
+  __shared__ float s_part[4][TT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int e = blockIdx.x;
   if (do_logits && e < E) {
-    float acc[MOE_MAX_DECODE_TOKENS];
+    float acc[TT];
 #pragma unroll
-    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) acc[t] = 0.f;
+    for (int t = 0; t < TT; ++t) acc[t] = 0.f;
     const float* w = Wr + (size_t)e * d;
 #pragma unroll 4
     for (int i = tid * 4; i < d; i += 1024) {
       const float4 wv = *reinterpret_cast<const float4*>(w + i);
+      uint2 xv[TT];
 #pragma unroll
-      for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
-        if (t < T) {
-          const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * d + i);
-          acc[t] = fmaf(bf16_to_f32(xv.x & 0xFFFFu), wv.x, acc[t]);
-          acc[t] = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc[t]);
-          acc[t] = fmaf(bf16_to_f32(xv.y & 0xFFFFu), wv.z, acc[t]);
-          acc[t] = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc[t]);
-        }
+      for (int t = 0; t < TT; ++t) xv[t] = *reinterpret_cast<const uint2*>(x + (size_t)t * d + i);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        acc[t] = fmaf(bf16_to_f32(xv[t].x & 0xFFFFu), wv.x, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].x >> 16), wv.y, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].y & 0xFFFFu), wv.z, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].y >> 16), wv.w, acc[t]);
       }
     }
 #pragma unroll
-    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
-      if (t < T) {
-        const float s = wave_sum(acc[t]);
-        if (lane == 0) s_part[wave][t] = s;
-      }
+    for (int t = 0; t < TT; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0) s_part[wave][t] = s;
     }
     __syncthreads();
-    if (tid < T) {
+    if (tid < TT) {
       const float s = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
       logits[(size_t)tid * E + e] = s + (bias ? bias[e] : 0.f);
     }
@@ -154,73 +155,87 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// candidate (ka, ia) ranks before (kb, ib): larger key, then lower index
-__device__ __forceinline__ bool ranks_before(uint32_t ka, int ia, uint32_t kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
+// Wave-wide maximum of a 32-bit value (uniform result): DPP steps inside each
+// 16-lane row, then the four row maxima read as scalars.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
 }
 
-// Top-k of one token's E logits by one wave.  Lane l holds experts l + 64i.
-// Returns (in lanes 0..k-1) the selected ids and weights.
+// Top-k of one token's E logits by one wave (lane l holds experts l + 64i),
+// larger logit first and the lower index first among equal ones: k rounds,
+// each taking the largest remaining order key (a wave maximum) and, among
+// the entries holding it, the one with the lowest expert index (each lane's
+// candidate is its lowest-index entry with its largest key; the lowest index
+// overall is the first lane of the lowest slot i holding the maximum).
+// Lanes 0..k-1 return the ids in order and their softmax weights
+// exp(l_j - l_0) / sum.  PER = entries per lane, a compile-time bound on E/64.
+template <int PER>
 __device__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, int& my_id,
                           float& my_w) {
-  constexpr int MAXPER = MOE_MAX_EXPERTS / 64;
+  constexpr int MAXPER = PER;  // PER * 64 >= E
+  const int per = (E + 63) / 64;
   float v[MAXPER];
   uint32_t key[MAXPER];
-  const int per = (E + 63) / 64;
+  uint32_t avail = 0;  // bit i: entry i present and not yet chosen
 #pragma unroll
   for (int i = 0; i < MAXPER; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (i < per && e < E) ? L[e] : -INFINITY;
+    const bool present = i < per && e < E;
+    v[i] = present ? L[e] : 0.f;
     key[i] = order_key(v[i]);
+    if (present) avail |= 1u << i;
   }
-  uint32_t taken = 0;  // bit i: v[i] already selected (or absent)
-#pragma unroll
-  for (int i = 0; i < MAXPER; ++i)
-    if (!(i < per && lane + 64 * i < E)) taken |= 1u << i;
-  float top = 0.f;
+  float top = 0.f, my_v = 0.f;
   my_id = -1;
-  float my_v = 0.f;
   for (int j = 0; j < k; ++j) {
-    // lane-local best (absent and taken entries never win; a present entry
-    // always beats the initial sentinel, NaN included)
     uint32_t bk = 0u;
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    int bi = -1;
+    float bv = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && ranks_before(key[i], e, bk, bi)) {
-        bk = key[i];
-        bv = v[i];
-        bi = e;
-      }
+      const bool better = ((avail >> i) & 1u) && (bi < 0 || key[i] > bk);
+      bk = better ? key[i] : bk;
+      bi = better ? i : bi;
+      bv = better ? v[i] : bv;
     }
-    // wave argmax under the same rule
+    const uint32_t kmax = wave_max_u32(bi >= 0 ? bk : 0u);
+    int sel_lane = 0, sel_i = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint32_t ok = __shfl_xor(bk, o, 64);
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ranks_before(ok, oi, bk, bi)) {
-        bk = ok;
-        bv = ov;
-        bi = oi;
+    for (int i = 0; i < MAXPER; ++i) {
+      if (i < per) {
+        const uint64_t m = __ballot(bi == i && bk == kmax);
+        if (m) {
+          sel_lane = __ffsll((unsigned long long)m) - 1;
+          sel_i = i;
+          break;
+        }
       }
     }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (j == 0) top = bv;
+    const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), sel_lane));
+    if (lane == sel_lane) avail &= ~(1u << sel_i);
+    if (j == 0) top = val;
     if (lane == j) {
-      my_id = bi;
-      my_v = bv;
+      my_id = sel_lane + 64 * sel_i;
+      my_v = val;
     }
   }
-  // softmax over the selected k (lanes < k)
-  float ex = (lane < k) ? expf(my_v - top) : 0.f;
-  float den = wave_sum(ex);
+  const float ex = (lane < k) ? expf(my_v - top) : 0.f;
+  const float den = wave_sum(ex);
   my_w = ex / den;
 }
 
 // Generic top-k: wave per token.
+template <int PER>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -228,7 +243,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   if (t >= T) return;
   int id;
   float wt;
-  wave_topk(logits + (size_t)t * E, E, k, lane, id, wt);
+  wave_topk<PER>(logits + (size_t)t * E, E, k, lane, id, wt);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     w[(size_t)t * k + lane] = wt;
@@ -287,85 +302,41 @@ __device__ int block_exclusive_scan(int* a, int n, int* wave_tot) {
 }
 
 // ------------------------------------------------- decode: select + permute
-// One block of 1024 threads for T <= 8 tokens (T*k <= 64 rows), built from
-// parallel counts rather than serial reductions:
-//   1. every logit's rank inside its token = the number of logits that rank
-//      before it (P threads per logit share the count); ranks below k are
-//      the selection, already in output order;
+// One block of 8 waves for T <= 8 tokens (T*k <= 64 rows):
+//   1. wave t selects token t's top-k (k rounds of a wave maximum) and its
+//      softmax weights;
 //   2. the <= 64 selected rows sit one per lane of wave 0, which derives each
 //      row's in-expert rank, permuted position and slot from ~log2(E)
 //      ballots over the expert-id bits;
 //   3. every expert's count and offset is a count over the rows, held in
 //      registers.
 // Slots list the active experts in ascending id, then the shared expert.
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;  // one wave per decode token
 
-__device__ __forceinline__ float key_value(uint32_t key) {  // inverse of order_key
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
+template <int PER>
 __global__ __launch_bounds__(kSelThreads) void k_dec_select(
     const float* __restrict__ logits, int T, int E, int k, int n_shared,
     int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_tok, int32_t* __restrict__ inv_row,
     int32_t* __restrict__ slots, int max_slots) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_key[MOE_MAX_DECODE_TOKENS * MOE_MAX_EXPERTS];
   __shared__ __attribute__((aligned(16))) int s_row[kDecodeMaxRoutedRows];  // expert of row t*k + j
-  __shared__ float s_selv[kDecodeMaxRoutedRows];
   __shared__ int s_nact;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = T * E, rows = T * k;
-  for (int i = tid; i < n; i += kSelThreads) s_key[i] = order_key(logits[i]);
-  __syncthreads();
-  // 1. ranks; P consecutive lanes per logit, each counting over E/P of its row
-  int P = 1;
-  while (P < 16 && 2 * P * n <= kSelThreads) P *= 2;
-  const int chunk = (E + P - 1) / P;
-  for (int base = 0; base < n * P; base += kSelThreads) {
-    const int idx = base + tid, i = idx / P, part = idx % P;
-    int rank = 0;
-    int t = 0, e = 0;
-    if (i < n) {
-      t = i / E;
-      e = i - t * E;
-      const uint32_t kv = s_key[i];
-      const uint32_t* row = s_key + t * E;
-      const int f0 = part * chunk, f1 = min(E, f0 + chunk);
-      int f = f0;
-      if (((t * E + f0) & 3) == 0) {
-        for (; f + 16 <= f1; f += 16) {
-          uint4 o[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) o[u] = *reinterpret_cast<const uint4*>(row + f + 4 * u);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            rank += ranks_before(o[u].x, f + 4 * u, kv, e) +
-                    ranks_before(o[u].y, f + 4 * u + 1, kv, e) +
-                    ranks_before(o[u].z, f + 4 * u + 2, kv, e) +
-                    ranks_before(o[u].w, f + 4 * u + 3, kv, e);
-        }
-      }
-      for (; f < f1; ++f) rank += ranks_before(row[f], f, kv, e);
-    }
-    for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
-    if (i < n && part == 0 && rank < k) {
-      s_row[t * k + rank] = e;
-      s_selv[t * k + rank] = key_value(s_key[i]);
-    }
-  }
-  __syncthreads();
-  // 2a. weights: softmax over each token's k selected logits (wave t)
+  const int rows = T * k;
+  // 1. top-k and weights, wave t for token t (same order and softmax as the
+  //    generic top-k kernel)
   if (wave < T) {
-    const int t = wave;
-    const float top = s_selv[t * k];
-    const float ex = lane < k ? expf(s_selv[t * k + lane] - top) : 0.f;
-    const float den = wave_sum(ex);
+    int id;
+    float w;
+    wave_topk<PER>(logits + (size_t)wave * E, E, k, lane, id, w);
     if (lane < k) {
-      ids[t * k + lane] = s_row[t * k + lane];
-      wts[t * k + lane] = ex / den;
+      ids[wave * k + lane] = id;
+      wts[wave * k + lane] = w;
+      s_row[wave * k + lane] = id;
     }
   }
-  // 2b. rows (wave 0): rank among the rows of the same expert, permuted
+  __syncthreads();
+  // 2. rows (wave 0): rank among the rows of the same expert, permuted
   //     position and slot, from ballots over the expert-id bits
   if (wave == 0) {
     const bool act = lane < rows;
@@ -580,8 +551,20 @@ int launch_route_generic(const moe_layer* L, const uint16_t* x, int T, uint32_t 
     hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
                        L->router_bias, R->logits, 1, (uint16_t*)nullptr, (uint16_t*)nullptr);
   }
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, R->logits, T, E, k, R->topk_ids,
-                     R->topk_w);
+#define BQ_TK(PER)                                                                              \
+  hipLaunchKernelGGL(k_topk<PER>, dim3((T + 3) / 4), dim3(256), 0, s, R->logits, T, E, k,      \
+                     R->topk_ids, R->topk_w)
+  if (E <= 64)
+    BQ_TK(1);
+  else if (E <= 128)
+    BQ_TK(2);
+  else if (E <= 256)
+    BQ_TK(4);
+  else if (E <= 512)
+    BQ_TK(8);
+  else
+    BQ_TK(16);
+#undef BQ_TK
   int32_t* hist = (int32_t*)(ws + P.hist);
   int32_t* lrank = (int32_t*)(ws + P.lrank);
   hipLaunchKernelGGL(k_hist, dim3(P.nblk), dim3(256), 0, s, R->topk_ids, T, E, k, hist, lrank);
@@ -602,15 +585,35 @@ int launch_decode_route(const moe_layer* L, const uint16_t* x, int T, uint32_t f
   if (mask & MOE_DECODE_STAGE_ROUTE) {
     const int G = d / 32;
     dim3 grid(max(E, (T * G + 7) / 8));
-    hipLaunchKernelGGL(k_dec_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
-                       L->router_bias, R->logits, do_logits, (uint16_t*)(ws + W.xs),
-                       (uint16_t*)(ws + W.xsum));
+#define BQ_LG(TT)                                                                             \
+  case TT:                                                                                    \
+    hipLaunchKernelGGL(k_dec_logits<TT>, grid, dim3(256), 0, s, x, T, d, E, L->router_w,      \
+                       L->router_bias, R->logits, do_logits, (uint16_t*)(ws + W.xs),          \
+                       (uint16_t*)(ws + W.xsum));                                             \
+    break
+    switch (T) {
+      BQ_LG(1); BQ_LG(2); BQ_LG(3); BQ_LG(4); BQ_LG(5); BQ_LG(6); BQ_LG(7); BQ_LG(8);
+      default: return (int)hipErrorInvalidValue;
+    }
+#undef BQ_LG
   }
-  if (mask & MOE_DECODE_STAGE_SELECT)
-    hipLaunchKernelGGL(k_dec_select, dim3(1), dim3(kSelThreads), 0, s, R->logits, T, E, k,
-                       L->n_shared,
-                       R->topk_ids, R->topk_w, R->counts, R->offsets, R->perm_tok, R->inv_row,
-                       (int32_t*)(ws + W.slots), W.max_slots);
+  if (mask & MOE_DECODE_STAGE_SELECT) {
+#define BQ_SEL(PER)                                                                               \
+  hipLaunchKernelGGL(k_dec_select<PER>, dim3(1), dim3(kSelThreads), 0, s, R->logits, T, E, k,    \
+                     L->n_shared, R->topk_ids, R->topk_w, R->counts, R->offsets, R->perm_tok,    \
+                     R->inv_row, (int32_t*)(ws + W.slots), W.max_slots)
+    if (E <= 64)
+      BQ_SEL(1);
+    else if (E <= 128)
+      BQ_SEL(2);
+    else if (E <= 256)
+      BQ_SEL(4);
+    else if (E <= 512)
+      BQ_SEL(8);
+    else
+      BQ_SEL(16);
+#undef BQ_SEL
+  }
   return (int)hipGetLastError();
 }
 

@@ -171,6 +171,42 @@ def test_decode_is_deterministic(layers):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["c0", "c1", "c2"])
+def test_decode_stages_one_by_one_and_rerun(layers, name):
+    """The decode stages run one call at a time match the oracle, and
+    re-running the two projection stages on the same workspace reproduces the
+    full call's output bit for bit (no state carried between launches)."""
+    dl = layers(name)
+    cfg = dl.cfg
+    x_np = synth.gen_x(cfg)
+    T = x_np.shape[0]
+    x = _to_dev_u16(x_np)
+    R = bq.alloc_routing(T, cfg.E, cfg.k, DEV)
+    ws = bq.alloc_workspace(dl.handle, T, DEV)
+    out = torch.empty((T, cfg.d), dtype=torch.int16, device=DEV)
+    print(f"[{name}] decode stages one by one", flush=True)
+    for st in (bq.MOE_DECODE_STAGE_ROUTE, bq.MOE_DECODE_STAGE_SELECT,
+               bq.MOE_DECODE_STAGE_GATEUP, bq.MOE_DECODE_STAGE_DOWN):
+        bq.moe_forward_decode_stages(dl.handle, x, T, 0, R, ws, out, st)
+    torch.cuda.synchronize()
+    staged = _host_u16(out).copy()
+    rt = _routing_host(R, T, cfg.k)
+    check_routing_exact(cfg, rt["logits"], rt)
+    ref = oracle_outputs(cfg, dl.layer, x_np, rt["logits"], np.arange(T), False)
+    assert_parity(staged, ref, f"{name} staged")
+    print(f"[{name}] full call, then the projection stages twice", flush=True)
+    bq.moe_forward_decode(dl.handle, x, T, 0, R, ws, out)
+    torch.cuda.synchronize()
+    full = _host_u16(out).copy()
+    assert np.array_equal(full, staged)
+    both = bq.MOE_DECODE_STAGE_GATEUP | bq.MOE_DECODE_STAGE_DOWN
+    for rep in range(2):
+        out.zero_()
+        bq.moe_forward_decode_stages(dl.handle, x, T, 0, R, ws, out, both)
+        torch.cuda.synchronize()
+        assert np.array_equal(_host_u16(out), full), rep
+
+
 def test_c3_prefill_full_sampled(layers):
     dl = layers("c3")
     cfg = dl.cfg
