@@ -40,6 +40,16 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+// 32x32x16 bf16 matrix-core op (gfx950): lane l supplies A[l%32][8(l/32)..+7]
+// and B[8(l/32)..+7][l%32]; it receives D[8(i/4) + 4(l/32) + i%4][l%32],
+// i = 0..15.  Measured on this chip at about 1.6 times the throughput of the
+// 16x16x32 op.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32x32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // Correction term of one 32-group as a zero-padded 16x16x32 op (the same
 // shape as the main op, which takes it as its C operand).  Lanes 0..15 hold
 // their row's staged sums in k-slots 0..7 of A: (-W, -S) as two negated bf16

@@ -3,16 +3,20 @@
 // expert's packed weights are a dense contraction (the "Xolotl" README, "What
 // one PC can do", measures prefill over 6K-17K-token prompts).
 //
-// A block takes one tile of <= 128 rows of one expert (the tile list comes from
-// the routing kernels) and 4 waves, each wave owning 4 (projection, 16-column
-// n-tile) pairs for all 8 row tiles of the block.  Per 128-wide k-block:
-//   - the block stages the 128 rows of pre-scaled activations (x/16 or h/16)
-//     and their 32-group sums in LDS (double-buffered through registers);
-//   - each wave reads its packed tiles straight from global memory: a tile's
-//     lane chunk is exactly the lane's B operand, so no LDS is needed for B;
-//     levels become the bf16 value 128 + 16u with a shift, a mask and an or;
-//   - per 32-group: C = -(8 + offset) * sum(x) by a zero-padded 16x16x32 op,
-//     D = A*B + C by 16x16x32 ops, acc += scale * D in fp32.
+// A block takes one tile of <= 64 rows of one expert (the tile list comes from
+// the routing kernels) and one group of output columns, with 4 waves; each
+// wave computes both 32-row halves of the tile against its own columns (gate
+// and up: 32 columns of each; down: 64 columns) with 32x32x16 matrix-core ops.
+// Per 128-wide k-block:
+//   - the block stages the 64 rows of pre-scaled activations (x/16 or h/16)
+//     and their 32-group sums in LDS with direct global->LDS loads
+//     (double-buffered: k-block kb+1 lands while kb is used);
+//   - each wave reads its packed tiles straight from global memory into
+//     registers one k-block ahead: a lane's 8-byte code chunks are exactly its
+//     B operand, so no LDS is needed for B; levels become bf16 values
+//     base + 16u with one mask-and-or per pair;
+//   - per 32-group: C = the correction term by a zero-padded op on the staged
+//     sums, D = A*B + C by two 32x32x16 ops, acc += scale * D in fp32.
 // Epilogues: gate/up -> h = bf16(SiLU(g) * u), stored as h/16 with the 32-group
 // sums of h for the down projection; down -> y = bf16(acc).
 #include <hip/hip_runtime.h>
@@ -22,8 +26,7 @@
 
 namespace bqmoe {
 
-constexpr int kRows = kPrefillTileM;  // rows per tile = 16 * RT
-constexpr int RT = kRows / 16;        // 16-row tiles per wave
+constexpr int kRows = kPrefillTileM;  // rows per tile (two 32-row matrix-core tiles)
 
 __device__ __forceinline__ float silu_pf(float g) { return g / (1.0f + expf(-g)); }
 
@@ -49,14 +52,6 @@ __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ x, i
   }
 }
 
-template <bool Q3, int GB>
-__device__ __forceinline__ u32x4 unpack_b(u32x2 w0, uint32_t w1) {
-  const uint32_t word = (GB < 2) ? w0[0] : w0[1];
-  if constexpr (Q3)
-    return unpack3<GB>(word, w1);
-  else
-    return unpack2<GB & 1>(word);
-}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -75,14 +70,18 @@ constexpr int kDmaA = 16 * kRows / 64;   // activation DMA instructions per k-bl
 constexpr int kDmaS = 4;                  // group-sum DMA instructions per k-block (one per group)
 static_assert(kRows == 64 && kDmaA % 4 == 0, "one row per lane in the group-sum loads");
 
-template <int NMAT, int NTPW, bool Q3A, bool Q3B, bool SAMEC>
+// NMAT = 2: gate/up, wave w of column group c covers columns
+//   [32 (4c + w), +32) of gate (column tile 0) and of up (column tile 1);
+// NMAT = 1: down, wave w covers columns [64 (4c + w), +64) (two column tiles).
+// Each wave computes both 32-row tiles of the block's 64 rows, so one 32x32
+// output tile per (row tile, column tile): 4 accumulators of 16 values.
+template <int NMAT, bool Q3A, bool Q3B, bool SAMEC>
 __global__ __launch_bounds__(256, 2) void k_pf_gemm(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ tiles, const int32_t* __restrict__ ctrl,
     const int32_t* __restrict__ perm_tok, int Tk, int gather, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Asum, int K, int N, float ca, float cb,
     uint16_t* __restrict__ out, uint16_t* __restrict__ out_sum, int ncol, Unpack2K uk) {
-  static_assert(NMAT * NTPW == 4, "four (projection, n-tile) streams per wave");
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * kBufBytes];
   __shared__ int sTok[kRows];
 
@@ -99,7 +98,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
   const int32_t* tl = tiles + 4 * tile;
   const int e = tl[0], row0 = tl[1], M = tl[2];
   const uint8_t* blob = e >= 0 ? experts + (size_t)e * stride : shared;
-  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hl = lane >> 5, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = K / 128, G = K / 32;
 
@@ -114,30 +113,39 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
   const uint16_t* arow[kRows / 64];
 #pragma unroll
   for (int h = 0; h < kRows / 64; ++h) arow[h] = A + (size_t)sTok[64 * h + lane] * K;
-  // group sums, stored group-major in LDS ([group][row][16 B]: the 16 rows a
+  // group sums, stored group-major in LDS ([group][row][16 B]: the rows a
   // matrix-core read touches are contiguous, free of bank conflicts); wave w
   // loads group w of the k-block, one row per lane
   const uint16_t* srow = Asum + ((size_t)sTok[lane] * G + (wave & 3)) * 8;
 
-  // this wave's streams: stream j -> projection (j / NTPW), n-tile nt0 + j % NTPW
-  const int nt0 = (col * 4 + wave) * NTPW;
+  // this wave's column tiles: projection and the n-tile holding this lane's column
+  const int cw = col * 4 + wave;
   const uint8_t* const base0 = blob + pa.off;
   const uint8_t* const base1 = blob + pb.off;
   const size_t scl0 = pa.scales, scl1 = pb.scales, pl0 = pa.plane1, pl1 = pb.plane1;
+  int ntl[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) ntl[ct] = (NMAT == 2 ? cw * 2 : cw * 4 + 2 * ct) + (l32 >> 4);
 
   const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1), lane_copy(uk.b2)};
-  const u32x4 bc0 = corr_b_operand(q == 0, Q3A, ca);
-  const u32x4 bc1 = corr_b_operand(q == 0, Q3B, cb);
+  // correction B operand: k-slots 0..7 (lanes 0..31) carry the constants
+  const u32x4 bc0 = corr_b_operand(lane < 32, Q3A, ca);
+  const u32x4 bc1 = corr_b_operand(lane < 32, Q3B, cb);
 
-  f32x4 acc[RT][4];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rt][ct][i] = 0.f;
 
-  // packed tiles of the k-block being used (c*) and of the next one, in flight (n*)
-  u32x2 cw[4], cs[4], nw[4], ns[4];
-  uint32_t ch[4], nh[4];
+  // packed tiles of the k-block being used (c*) and of the next one (n*): per
+  // column tile, the lane's two 8-B code chunks (k-slots 8(2h + lane/32) ..+7
+  // of each group, h = 0, 1), its column's 4 group scales, and for 3-bit
+  // levels the two level-bit-2 words
+  u32x2 cw_[2][2], cs_[2], nw_[2][2], ns_[2];
+  uint32_t ch_[2][2], nh_[2][2];
 
 #define BQ_ISSUE(KB_, BUF_)                                                                    \
   {                                                                                            \
@@ -155,33 +163,35 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
                                        (lds_void*)(dst + kRows * 256 + wave * 1024), 16, 0, 0); \
   }
 
-#define BQ_LOADB(KB_, S_)                                                                      \
+#define BQ_LOADB(KB_, W_, S_, H_)                                                              \
   {                                                                                            \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                            \
-      const bool first = (j / NTPW == 0);                                                      \
-      const uint8_t* bb = first ? base0 : base1;                                               \
-      const size_t tile = (size_t)(nt0 + (j % NTPW)) * KB + (KB_);                             \
-      S_##w[j] = *reinterpret_cast<const u32x2*>(bb + tile * 512 + lane * 8);                  \
-      S_##s[j] = *reinterpret_cast<const u32x2*>(bb + (first ? scl0 : scl1) + tile * 128 +     \
-                                                 r * 8);                                       \
-      const bool q3 = first ? Q3A : Q3B;                                                       \
-      S_##h[j] = q3 ? *reinterpret_cast<const uint32_t*>(bb + (first ? pl0 : pl1) +            \
-                                                         tile * 256 + lane * 4)                \
-                    : 0u;                                                                      \
+    _Pragma("unroll") for (int ct = 0; ct < 2; ++ct) {                                         \
+      const bool sec = NMAT == 2 && ct == 1;                                                   \
+      const uint8_t* bb = sec ? base1 : base0;                                                 \
+      const size_t tile_ = (size_t)ntl[ct] * KB + (KB_);                                       \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
+        const int chunk_ = 16 * (2 * h + hl) + r;                                              \
+        W_[ct][h] = *reinterpret_cast<const u32x2*>(bb + tile_ * 512 + chunk_ * 8);            \
+        H_[ct][h] = (sec ? Q3B : Q3A)                                                          \
+                        ? *reinterpret_cast<const uint32_t*>(bb + (sec ? pl1 : pl0) +          \
+                                                             tile_ * 256 + chunk_ * 4)         \
+                        : 0u;                                                                  \
+      }                                                                                        \
+      S_[ct] = *reinterpret_cast<const u32x2*>(bb + (sec ? scl1 : scl0) + tile_ * 128 + r * 8); \
     }                                                                                          \
   }
 
   // k-block kb: wait for its activations (LDS) and tiles (registers), then
   // issue k-block kb+1 into the other buffer and register set, then compute
   BQ_ISSUE(0, 0)
-  BQ_LOADB(0, c)
+  BQ_LOADB(0, cw_, cs_, ch_)
   for (int kb = 0; kb < KB; ++kb) {
     const int buf = kb & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // k-block kb is in LDS for every wave; buffer buf^1 is free
     if (kb + 1 < KB) {
       BQ_ISSUE(kb + 1, buf ^ 1)
-      BQ_LOADB(kb + 1, n)
+      BQ_LOADB(kb + 1, nw_, ns_, nh_)
     }
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* sA = sbuf + buf * kBufBytes;
@@ -189,38 +199,42 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
 
 #define BQ_PF_GROUP(GB)                                                                         \
   {                                                                                             \
-    /* the group's LDS reads first (all row tiles), so that their latency runs */              \
-    /* under the unpacking below rather than in front of each matrix-core op */                \
-    u32x4 av[RT], aa[RT];                                                                       \
-    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                         \
-      /* lanes q != 0 meet zeros in the correction B operand: no select needed */              \
-      av[rt] = *reinterpret_cast<const u32x4*>(sS + GB * kColBytes + (rt * 16 + r) * 16);       \
-      aa[rt] = *reinterpret_cast<const u32x4*>(sA + (GB * 4 + q) * kColBytes + (rt * 16 + r) * 16); \
+    /* the group's LDS reads first, so that their latency runs under the unpacking */          \
+    u32x4 aa[2][2], av[2];                                                                      \
+    _Pragma("unroll") for (int rt = 0; rt < 2; ++rt) {                                          \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h) aa[rt][h] =                                 \
+          *reinterpret_cast<const u32x4*>(sA + (GB * 4 + 2 * h + hl) * kColBytes +             \
+                                          (rt * 32 + l32) * 16);                                \
+      /* lanes 32..63 meet zeros in the correction B operand: any value is fine */             \
+      av[rt] = *reinterpret_cast<const u32x4*>(sS + GB * kColBytes + (rt * 32 + l32) * 16);    \
     }                                                                                           \
     __builtin_amdgcn_sched_barrier(0);                                                          \
-    u32x4 b[4];                                                                                 \
-    float sc[4];                                                                                \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                             \
-      const bool q3 = (j / NTPW == 0) ? Q3A : Q3B;                                              \
-      if (q3)                                                                                   \
-        b[j] = unpack_b<true, GB>(cw[j], ch[j]);                                                \
-      else                                                                                      \
-        b[j] = unpack2_r<GB & 1>((GB < 2) ? cw[j][0] : cw[j][1], ur);                           \
-      const uint32_t sbits = ((GB < 2) ? cs[j][0] : cs[j][1]) >> (16 * (GB & 1));               \
-      sc[j] = f16_to_f32(sbits & 0xFFFFu);                                                      \
+    u32x4 b[2][2];                                                                              \
+    float sc[2];                                                                                \
+    _Pragma("unroll") for (int ct = 0; ct < 2; ++ct) {                                          \
+      const bool q3 = (NMAT == 2 && ct == 1) ? Q3B : Q3A;                                       \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                           \
+        const uint32_t word = (GB < 2) ? cw_[ct][h][0] : cw_[ct][h][1];                        \
+        if (q3)                                                                                 \
+          b[ct][h] = unpack3<GB>(word, ch_[ct][h]);                                             \
+        else                                                                                    \
+          b[ct][h] = unpack2_r<GB & 1>(word, ur);                                               \
+      }                                                                                         \
+      const uint32_t sbits = ((GB < 2) ? cs_[ct][0] : cs_[ct][1]) >> (16 * (GB & 1));           \
+      sc[ct] = f16_to_f32(sbits & 0xFFFFu);                                                     \
       /* an fp32 register: plain FMAs below rather than mixed-precision ones */                 \
-      asm volatile("" : "+v"(sc[j]));                                                           \
+      asm volatile("" : "+v"(sc[ct]));                                                          \
     }                                                                                           \
-    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                         \
-      const f32x4 corr0 = mfma_corr(av[rt], bc0);                                               \
-      f32x4 corr1 = corr0;                                                                      \
-      if constexpr (!SAMEC) corr1 = mfma_corr(av[rt], bc1);                                     \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                           \
-        const f32x4 dd = mfma32(aa[rt], b[j], (j / NTPW == 0) ? corr0 : corr1);                 \
-        acc[rt][j][0] = fmaf(sc[j], dd[0], acc[rt][j][0]);                                      \
-        acc[rt][j][1] = fmaf(sc[j], dd[1], acc[rt][j][1]);                                      \
-        acc[rt][j][2] = fmaf(sc[j], dd[2], acc[rt][j][2]);                                      \
-        acc[rt][j][3] = fmaf(sc[j], dd[3], acc[rt][j][3]);                                      \
+    _Pragma("unroll") for (int rt = 0; rt < 2; ++rt) {                                          \
+      const f32x16 zero = {};                                                                   \
+      const f32x16 corr0 = mfma32x32(av[rt], bc0, zero);                                        \
+      f32x16 corr1 = corr0;                                                                     \
+      if constexpr (!SAMEC) corr1 = mfma32x32(av[rt], bc1, zero);                               \
+      _Pragma("unroll") for (int ct = 0; ct < 2; ++ct) {                                        \
+        f32x16 d = mfma32x32(aa[rt][0], b[ct][0], (NMAT == 2 && ct == 1) ? corr1 : corr0);      \
+        d = mfma32x32(aa[rt][1], b[ct][1], d);                                                  \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i)                                          \
+            acc[rt][ct][i] = fmaf(sc[ct], d[i], acc[rt][ct][i]);                                \
       }                                                                                         \
     }                                                                                           \
   }
@@ -234,60 +248,57 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
 #undef BQ_PF_GROUP
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      cw[j] = nw[j];
-      cs[j] = ns[j];
-      ch[j] = nh[j];
+    for (int ct = 0; ct < 2; ++ct) {
+      cs_[ct] = ns_[ct];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        cw_[ct][h] = nw_[ct][h];
+        ch_[ct][h] = nh_[ct][h];
+      }
     }
   }
 #undef BQ_ISSUE
 #undef BQ_LOADB
 
   // ------------------------------------------------------------ epilogues
+  // acc[rt][ct][i] is row rt*32 + 8(i/4) + 4(lane/32) + i%4, column l32 of
+  // column tile ct
   if constexpr (NMAT == 2) {
-    // streams 0..NTPW-1 are gate n-tiles, NTPW..2*NTPW-1 the matching up n-tiles;
-    // the wave's 2*16 = 32 columns form one 32-group of the down projection
+    // gate (tile 0) and up (tile 1) of the same 32 columns of I: one 32-group
+    // of the down projection
     const int I = N;
+    const float wgt = slot_weight(l32);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = rt * 16 + 4 * q + i;
-        float hs_part = 0.f, hw_part = 0.f;
-        const float wgt = slot_weight(r);  // column nt*16 + r is k-slot (16 jn + r) of its group
+      for (int i = 0; i < 16; ++i) {
+        const int m = rt * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+        const float g = acc[rt][0][i], u = acc[rt][1][i];
+        const float hf = bf16_to_f32(f32_to_bf16(silu_pf(g) * u));
+        if (m < M) out[(size_t)(row0 + m) * I + cw * 32 + l32] = (uint16_t)f32_to_bf16(hf * 0.0625f);
+        float hs_part = hf, hw_part = hf * wgt;
+        // sum over the 32 lanes holding this row (columns 0..31)
 #pragma unroll
-        for (int jn = 0; jn < NTPW; ++jn) {
-          const float g = acc[rt][jn][i], u = acc[rt][NTPW + jn][i];
-          const uint32_t hb = f32_to_bf16(silu_pf(g) * u);
-          const float hf = bf16_to_f32(hb);
-          hs_part += hf;
-          hw_part += hf * wgt;
-          if (m < M)
-            out[(size_t)(row0 + m) * I + (nt0 + jn) * 16 + r] = (uint16_t)f32_to_bf16(hf * 0.0625f);
+        for (int o = 16; o > 0; o >>= 1) {
+          hs_part += __shfl_xor(hs_part, o, 32);
+          hw_part += __shfl_xor(hw_part, o, 32);
         }
-        // sum over the 16 lanes holding this row (r = 0..15)
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-          hs_part += __shfl_xor(hs_part, o, 16);
-          hw_part += __shfl_xor(hw_part, o, 16);
-        }
-        if (m < M && r == 0) {
-          const int g32 = (nt0 * 16) / 32;
-          *reinterpret_cast<uint4*>(out_sum + ((size_t)(row0 + m) * (I / 32) + g32) * 8) =
+        if (m < M && l32 == 0)
+          *reinterpret_cast<uint4*>(out_sum + ((size_t)(row0 + m) * (I / 32) + cw) * 8) =
               stage_sums(hw_part, hs_part);
-        }
       }
     }
   } else {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = rt * 16 + 4 * q + i;
+      for (int i = 0; i < 16; ++i) {
+        const int m = rt * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
         if (m < M) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            out[(size_t)(row0 + m) * N + (nt0 + j) * 16 + r] = (uint16_t)f32_to_bf16(acc[rt][j][i]);
+          for (int ct = 0; ct < 2; ++ct)
+            out[(size_t)(row0 + m) * N + cw * 64 + ct * 32 + l32] =
+                (uint16_t)f32_to_bf16(acc[rt][ct][i]);
         }
       }
   }
@@ -377,7 +388,7 @@ template <bool A3, bool B3, bool SAMEC>
 static void launch_gu(dim3 grid, hipStream_t s, const moe_layer* L, ProjDesc pg, ProjDesc pu,
                       const int32_t* tiles, const int32_t* ctrl, const int32_t* perm_tok, int Tk,
                       const uint16_t* xs, const uint16_t* xsum, uint16_t* hs, uint16_t* hsum) {
-  hipLaunchKernelGGL((k_pf_gemm<2, 2, A3, B3, SAMEC>), grid, dim3(256), 0, s, (const uint8_t*)L->experts,
+  hipLaunchKernelGGL((k_pf_gemm<2, A3, B3, SAMEC>), grid, dim3(256), 0, s, (const uint8_t*)L->experts,
                      L->expert_stride, (const uint8_t*)L->shared, pg, pu, tiles, ctrl, perm_tok, Tk,
                      1, xs, xsum, L->d, L->inter, qtype_offset(L->q_gate), qtype_offset(L->q_up), hs,
                      hsum, L->inter / 128, kUnpack2);
@@ -424,12 +435,12 @@ int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
   const dim3 g2((unsigned)(((long)P.max_tiles * (d / 256) + 7) / 8 * 8));
   if (!(mask & MOE_PREFILL_STAGE_DOWN)) {
   } else if (L->q_down == MOE_Q_INT3)
-    hipLaunchKernelGGL((k_pf_gemm<1, 4, true, true, true>), g2, dim3(256), 0, s,
+    hipLaunchKernelGGL((k_pf_gemm<1, true, true, true>), g2, dim3(256), 0, s,
                        (const uint8_t*)L->experts, L->expert_stride, (const uint8_t*)L->shared, pdn,
                        pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hsum, I, d, qtype_offset(L->q_down),
                        qtype_offset(L->q_down), y, (uint16_t*)nullptr, d / 256, kUnpack2);
   else
-    hipLaunchKernelGGL((k_pf_gemm<1, 4, false, false, true>), g2, dim3(256), 0, s,
+    hipLaunchKernelGGL((k_pf_gemm<1, false, false, true>), g2, dim3(256), 0, s,
                        (const uint8_t*)L->experts, L->expert_stride, (const uint8_t*)L->shared, pdn,
                        pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hsum, I, d, qtype_offset(L->q_down),
                        qtype_offset(L->q_down), y, (uint16_t*)nullptr, d / 256, kUnpack2);

@@ -16,66 +16,42 @@ namespace bqmoe {
 // ------------------------------------------------------------------ logits
 // Wave per expert, up to 8 tokens per block row (grid.y tiles the tokens).
 // Router weights are stored [E][d] so a wave streams one contiguous row.
-// With `xs` set (decode), blocks also stage x for the expert kernels:
-// xs = x/16 (exact) and, per 32-group, the sums W and S of the correction
-// term (see stage_sums in device_common.h).
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x, int T, int d,
                                                        int E, const float* __restrict__ Wr,
                                                        const float* __restrict__ bias,
-                                                       float* __restrict__ logits, int do_logits,
-                                                       uint16_t* __restrict__ xs,
-                                                       uint16_t* __restrict__ xsum) {
+                                                       float* __restrict__ logits) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.y * 8;
   const int nt = min(8, T - t0);
-  if (do_logits) {
-    const int e = blockIdx.x * 4 + wave;
-    if (e < E) {
-      float acc[8];
+  const int e = blockIdx.x * 4 + wave;
+  if (e >= E) return;
+  // rows past the last token re-read the last token (their sums are not
+  // stored), so that every load of a step is unconditional
+  const uint16_t* xr[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] = 0.f;
-      const float* w = Wr + (size_t)e * d;
-      for (int i = lane * 4; i < d; i += 256) {
-        const float4 wv = *reinterpret_cast<const float4*>(w + i);
+  for (int t = 0; t < 8; ++t) xr[t] = x + (size_t)(t0 + min(t, nt - 1)) * d;
+  float acc[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          if (t < nt) {
-            const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + t) * d + i);
-            acc[t] = fmaf(bf16_to_f32(xv.x & 0xFFFFu), wv.x, acc[t]);
-            acc[t] = fmaf(bf16_to_f32(xv.x >> 16), wv.y, acc[t]);
-            acc[t] = fmaf(bf16_to_f32(xv.y & 0xFFFFu), wv.z, acc[t]);
-            acc[t] = fmaf(bf16_to_f32(xv.y >> 16), wv.w, acc[t]);
-          }
-        }
-      }
-      const float b = bias ? bias[e] : 0.f;
+  for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+  const float* w = Wr + (size_t)e * d;
+  for (int i = lane * 4; i < d; i += 256) {
+    const float4 wv = *reinterpret_cast<const float4*>(w + i);
+    uint2 xv[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (t < nt) {
-          const float s = wave_sum(acc[t]);
-          if (lane == 0) logits[(size_t)(t0 + t) * E + e] = s + b;
-        }
-      }
+    for (int t = 0; t < 8; ++t) xv[t] = *reinterpret_cast<const uint2*>(xr[t] + i);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc[t] = fmaf(bf16_to_f32(xv[t].x & 0xFFFFu), wv.x, acc[t]);
+      acc[t] = fmaf(bf16_to_f32(xv[t].x >> 16), wv.y, acc[t]);
+      acc[t] = fmaf(bf16_to_f32(xv[t].y & 0xFFFFu), wv.z, acc[t]);
+      acc[t] = fmaf(bf16_to_f32(xv[t].y >> 16), wv.w, acc[t]);
     }
   }
-  if (xs) {
-    // staging: one 32-lane half-wave per (token, group); pairs spread over the grid
-    const int G = d / 32;
-    const int pairs = T * G;
-    const int half = threadIdx.x >> 5, j = threadIdx.x & 31;
-    for (int p = blockIdx.x * 8 + half; p < pairs; p += gridDim.x * 8) {
-      const int t = p / G, g = p % G;
-      const uint32_t xb = x[(size_t)t * d + g * 32 + j];
-      const float xf = bf16_to_f32(xb);
-      xs[(size_t)t * d + g * 32 + j] = (uint16_t)f32_to_bf16(xf * 0.0625f);
-      float sw = xf * slot_weight(j), s = xf;
+  const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) {
-        sw += __shfl_xor(sw, o, 32);
-        s += __shfl_xor(s, o, 32);
-      }
-      if (j == 0) *reinterpret_cast<uint4*>(xsum + ((size_t)t * G + g) * 8) = stage_sums(sw, s);
-    }
+  for (int t = 0; t < 8; ++t) {
+    const float s = wave_sum(acc[t]);
+    if (t < nt && lane == 0) logits[(size_t)(t0 + t) * E + e] = s + b;
   }
 }
 
@@ -84,7 +60,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 // together): block per expert, its 4 waves split d; the router row is read
 // once for all T tokens and the partial sums meet in LDS.  The blocks also
 // stage x for the expert kernels: xs = x/16 (exact) and, per 32-group, the
-// staged sums.
+// staged sums of the correction term (see stage_sums in device_common.h).
 template <int TT>
 __global__ __launch_bounds__(256) void k_dec_logits(const uint16_t* __restrict__ x, int T, int d,
                                                     int E, const float* __restrict__ Wr,
@@ -549,7 +525,7 @@ int launch_route_generic(const moe_layer* L, const uint16_t* x, int T, uint32_t 
   if (!(flags & MOE_LOGITS_GIVEN)) {
     dim3 grid((E + 3) / 4, (T + 7) / 8);
     hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, T, d, E, L->router_w,
-                       L->router_bias, R->logits, 1, (uint16_t*)nullptr, (uint16_t*)nullptr);
+                       L->router_bias, R->logits);
   }
 #define BQ_TK(PER)                                                                              \
   hipLaunchKernelGGL(k_topk<PER>, dim3((T + 3) / 4), dim3(256), 0, s, R->logits, T, E, k,      \
