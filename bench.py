@@ -76,6 +76,10 @@ def parse():
                          "times")
     ap.add_argument("--loop-stage", default="gateup", choices=["gateup", "down"],
                     help="the stage --kernel-loop launches")
+    ap.add_argument("--extra", default="c2,c4",
+                    help="further workloads measured after the headline ones and reported in "
+                         "the same line: c2 (decode, 8 tokens), c4 (4-layer prefill stack); "
+                         "'none' skips them")
     ap.add_argument("--prefill-only", action="store_true",
                     help="profiling aid: run only the prefill leg and print its result")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -333,6 +337,7 @@ def main():
     if d is None:  # profiling loop only
         return
     pre = None if args.prefill_config == "none" else prefill_leg(args, dev)
+    extra = extra_legs(args, dev)
     cfg = d["cfg"]
     cpu = cpu_baseline(args, cfg, d["bytes_per_step"]) if args.cpu_seconds > 0 else None
     gbs = d["bytes_per_step"] / (d["ms"] * 1e-3) / 1e9
@@ -362,8 +367,33 @@ def main():
         "roofline": d["roof"],
         "cpu_baseline": cpu,
         "prefill": pre,
+        **extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def extra_legs(args, dev):
+    """C2 decode (8 tokens, 3/3/2-bit, Zipf-biased router) and the C4 prefill stack (4 layers,
+    16384 tokens, ternary, residual), each with a short run of its own."""
+    want = set(args.extra.split(",")) - {"none", ""}
+    out = {}
+    if "c2" in want:
+        a = argparse.Namespace(**vars(args))
+        a.config, a.steps, a.warmup, a.copies, a.kernel_loop = "c2", 50, 5, 4, 0
+        d = decode_leg(a, dev)
+        gbs = d["bytes_per_step"] / (d["ms"] * 1e-3) / 1e9
+        out["decode_c2"] = {
+            "workload": d["cfg"].name, "T": d["cfg"].T, "steps": a.steps, "layer_copies": a.copies,
+            "us_per_layer": d["ms"] * 1e3, "packed_expert_bytes_per_step": d["bytes_per_step"],
+            "unique_routed_experts_per_step": d["active"] - d["cfg"].n_shared,
+            "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "gateup_kernel_us": d["roof"]["avg_launch_us"],
+            "gateup_kernel_gbs": d["roof"]["achieved"]}
+    if "c4" in want:
+        a = argparse.Namespace(**vars(args))
+        a.prefill_config, a.prefill_steps = "c4", 2
+        out["prefill_c4"] = prefill_leg(a, dev)
+    return out
 
 
 def synth_qname(q):

@@ -9,15 +9,15 @@
 // rows; the column group is one 16-column n-tile of gate and of up (2
 // streams), or 4 n-tiles (64 output columns) of down (4 streams).  The
 // block's waves split the reduction dimension into contiguous k-block ranges,
-// each wave owning 16 (stream, k-block) tiles.  A wave
-//   1. copies its slice of the slot's M activation rows (pre-scaled by 1/16)
-//      and of their 32-group sums from global memory straight into its own
-//      LDS region,
-//   2. issues the loads of all its packed tiles,
-//   3. waits for the copies only (loads complete in issue order), and
-//   4. works through its k-blocks as their tiles arrive; per 32-group:
-//        A = the rows from LDS (lanes of rows >= M read row 0; those outputs
-//            are discarded),
+// each wave owning 16 (stream, k-block) tiles.  A wave works through its
+// k-blocks with the loads of the next one in flight:
+//   1. it fetches the k-block's M activation rows (pre-scaled by 1/16) and
+//      their 32-group sums into registers, with the k-block's packed tiles;
+//   2. it writes the rows and sums to its own small LDS buffer when the
+//      k-block's turn comes, and reads them back in matrix-operand order;
+//   3. per 32-group:
+//        A = the rows (lanes of rows >= M read row 0; those outputs are
+//            discarded),
 //        B = packed levels turned into bf16 values base + 16u by one
 //            mask-and-or per pair of levels (see device_common.h),
 //        C = the group's correction term (see mfma_corr in device_common.h),
@@ -25,6 +25,9 @@
 //      group's fp16 scale (2 bytes per lane, broadcast with a lane shuffle)
 //      and accumulated in fp32, only in the accumulator rows that hold real
 //      rows.
+// Every wait is placed by the compiler (no direct-to-LDS loads), and there
+// are no branches around the work on a k-block: a load whose only use sits in
+// a branch may be moved into it, which would undo the prefetch.
 // Partial sums of the waves meet in LDS in a fixed order: no floating-point
 // atomics, no cross-block synchronisation.
 #include <hip/hip_runtime.h>
@@ -42,63 +45,71 @@ constexpr int kDecMaxRows = 8;  // rows of one slot (<= T <= 8)
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-// LDS region of one wave: activation rows [M][KBW*128 bf16 + 16 B pad], then
-// staged sums [M][KBW*4][16 B]; each part rounded up to whole KB, as the
-// direct loads fill 1 KB per instruction.
-__host__ __device__ constexpr int dw_row_stride(int kbw) { return kbw * 256 + 16; }
-__host__ __device__ constexpr int dw_rows_bytes(int M, int kbw) {
-  return (M * dw_row_stride(kbw) + 1023) & ~1023;
-}
-__host__ __device__ constexpr int dw_sum_bytes(int M, int kbw) {
-  return (M * kbw * 64 + 1023) & ~1023;
-}
-__host__ __device__ constexpr int dw_bytes(int M, int kbw) {
-  return dw_rows_bytes(M, kbw) + dw_sum_bytes(M, kbw);
-}
-
 // ---------------------------------------------------------------- wave steps
-// 1. A wave's slice of its slot's M rows (k-blocks kb0 .. kb0+nkb of each row)
-//    and of their staged sums -> the wave's LDS region, by direct loads of
-//    1 KB each.  Row c of the slot is source row `base + c`, or with `gather`
-//    token (tok3 >> 3c) & 7 (decode tokens are < 8; no indexed array, which
-//    the compiler would place in scratch memory).  A lane whose bytes fall in
-//    a row's padding, past the slice or past the last row copies the first
-//    bytes of row 0 (never read).
+// Row c of a slot is source row `base + c`, or with `gather` token
+// (tok3 >> 3c) & 7 (decode tokens are < 8; no indexed array, which the
+// compiler would place in scratch memory).
 __device__ __forceinline__ int dec_src_row(int c, bool gather, int base, uint32_t tok3) {
   return gather ? (int)((tok3 >> (3 * c)) & 7u) : base + c;
 }
 
-template <int KBW>
-__device__ __forceinline__ void dec_stage_rows(uint8_t* sA, uint8_t* sS, int lane, int M,
-                                               bool gather, int base, uint32_t tok3,
-                                               const uint16_t* __restrict__ A,
-                                               const uint8_t* __restrict__ Asum, int K, int kb0,
-                                               int nkb) {
-  constexpr int RS = dw_row_stride(KBW), SS = KBW * 64;
+// 1. A k-block of a slot's rows passes through a small per-wave LDS buffer:
+//    rows [RC][256 B + 16 B pad] (the pad spreads the rows over the LDS
+//    banks), then their staged sums [RC][64 B]; RC is the row cap (1 for a
+//    single-token launch, else 8).  Rows >= M fetch row 0 (never read).  For
+//    the down projection the fetched (W, S) half sums are turned into staged
+//    sums on the way.
+__host__ __device__ constexpr int ring_row_stride() { return 256 + 16; }
+__host__ __device__ constexpr int ring_bytes(int rc) { return rc * (ring_row_stride() + 64); }
+// LDS of one wave, rounded to 256 B
+__host__ __device__ constexpr int ring_wave_bytes(int rc) { return (ring_bytes(rc) + 255) & ~255; }
+
+template <int RC>
+struct KbRegs {
+  u32x4 a[(RC * 16 + 63) / 64];  // 16-byte pieces of the rows, one per lane
+  u32x4 s;                       // one 32-group of one row (lanes < 4 RC)
+};
+
+template <int RC>
+__device__ __forceinline__ void dec_kb_fetch(KbRegs<RC>& v, int lane, int M, bool gather,
+                                             int base, uint32_t tok3,
+                                             const uint16_t* __restrict__ A,
+                                             const uint8_t* __restrict__ Asum, int K, int kb) {
   const int G = K / 32;
-  const int n_a = dw_rows_bytes(M, KBW) / 1024;
-  for (int i = 0; i < n_a; ++i) {
-    const int off = i * 1024 + lane * 16;
-    int c = off / RS;
-    const int within = off % RS;
-    const bool ok = c < M && within < nkb * 256;
-    c = ok ? c : 0;
+#pragma unroll
+  for (int p = 0; p < (RC * 16 + 63) / 64; ++p) {
+    const int piece = (p * 64 + lane) & (RC * 16 - 1);
+    int c = piece >> 4;
+    c = c < M ? c : 0;
     const int src = dec_src_row(c, gather, base, tok3);
-    const uint8_t* g =
-        reinterpret_cast<const uint8_t*>(A + (size_t)src * K) + (ok ? kb0 * 256 + within : 0);
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(sA + i * 1024), 16, 0, 0);
+    v.a[p] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(A + (size_t)src * K) +
+                                             kb * 256 + (piece & 15) * 16);
   }
-  const int n_s = dw_sum_bytes(M, KBW) / 1024;
-  for (int i = 0; i < n_s; ++i) {
-    const int off = i * 1024 + lane * 16;
-    int c = off / SS;
-    const int within = off % SS;
-    const bool ok = c < M && within < nkb * 64;
-    c = ok ? c : 0;
-    const int src = dec_src_row(c, gather, base, tok3);
-    const uint8_t* g = Asum + (size_t)src * G * 16 + (ok ? kb0 * 64 + within : 0);
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(sS + i * 1024), 16, 0, 0);
+  int c = (lane >> 2) & (RC - 1);
+  c = c < M ? c : 0;
+  const int src = dec_src_row(c, gather, base, tok3);
+  v.s = *reinterpret_cast<const u32x4*>(Asum + (size_t)src * G * 16 + (kb * 4 + (lane & 3)) * 16);
+}
+
+// Every lane stores (lanes past the pieces repeat a piece with the same
+// data): a store under a lane test would let the compiler move the fetch
+// into that branch, next to its only use.
+template <int RC, bool HALF_SUMS>
+__device__ __forceinline__ void dec_kb_store(uint8_t* buf, const KbRegs<RC>& v, int lane) {
+#pragma unroll
+  for (int p = 0; p < (RC * 16 + 63) / 64; ++p) {
+    const int piece = (p * 64 + lane) & (RC * 16 - 1);
+    *reinterpret_cast<u32x4*>(buf + (piece >> 4) * ring_row_stride() + (piece & 15) * 16) =
+        v.a[p];
   }
+  u32x4 sv = v.s;
+  if constexpr (HALF_SUMS) {
+    // (Wa, Sa, Wb, Sb): fp32 sums of h over the group's two 16-column halves
+    const uint4 st = stage_sums(__uint_as_float(sv[0]) + __uint_as_float(sv[2]),
+                                __uint_as_float(sv[1]) + __uint_as_float(sv[3]));
+    sv = u32x4{st.x, st.y, st.z, st.w};
+  }
+  *reinterpret_cast<u32x4*>(buf + RC * ring_row_stride() + (lane & (RC * 4 - 1)) * 16) = sv;
 }
 
 // 2. Packed tiles of one of a wave's k-blocks (kb0 + i) for NS streams: codes
@@ -137,47 +148,22 @@ __device__ __forceinline__ void dec_load_kb(int i, u32x2 (&wc)[KBW][NS], uint32_
   }
 }
 
-// 3. Wait until at most N vector-memory loads are outstanding.  Loads complete
-//    in issue order, so with the N tile loads issued after the copies into
-//    LDS, the copies have landed.
-template <int N>
-__device__ __forceinline__ void wait_for_copies() {
-  static_assert(N <= 63, "vmcnt holds at most 63 outstanding loads");
-  __builtin_amdgcn_sched_barrier(0);
-  // s_waitcnt vmcnt(N), expcnt and lgkmcnt at their maxima (no wait)
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// (Wa, Sa, Wb, Sb): fp32 sums of h over the two 16-column halves of each
-// 32-group -> staged sums of the group, in place (down projection)
-template <int KBW>
-__device__ __forceinline__ void dec_half_sums_to_staged(uint8_t* sS, int lane, int M, int nkb) {
-  constexpr int SS = KBW * 64;
-  for (int t = lane; t < M * KBW * 4; t += 64) {
-    const int m = t / (KBW * 4), g = t % (KBW * 4);
-    if (g < nkb * 4) {
-      uint8_t* p = sS + m * SS + g * 16;
-      const float4 v = *reinterpret_cast<const float4*>(p);
-      *reinterpret_cast<uint4*>(p) = stage_sums(v.x + v.z, v.y + v.w);
-    }
-  }
-}
-
-// 4. Matrix-core work on one k-block; per 32-group one correction op (two if
+// 3. Matrix-core work on one k-block; per 32-group one correction op (two if
 //    the projections differ) and one op per stream; the group's scale
 //    multiplies MR accumulator rows (rows 4*(lane/16) + i carry real rows for
-//    i < M; MR = 1 when M == 1).
-template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int MR>
+//    i < M; MR = 1 when M == 1).  A and the sums come from the k-block's LDS
+//    buffer.  GUARD: a k-block past the wave's range (live false) adds zero,
+//    through a zero scale.
+template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int MR, bool GUARD>
 __device__ __forceinline__ void dec_mfma_kb(int i, f32x4 (&acc)[NS], const u32x2 (&wc)[KBW][NS],
                                             const uint32_t (&wh)[KBW][NS],
                                             const uint32_t (&ws)[KBW][NS], const uint8_t* aptr,
                                             const uint8_t* sptr, u32x4 bca, u32x4 bcb,
-                                            const Unpack2R& ur, int r) {
+                                            const Unpack2R& ur, int r, bool live = true) {
 #pragma unroll
   for (int GB = 0; GB < 4; ++GB) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(aptr + (i * 128 + GB * 32) * 2);
-    const u32x4 sv = *reinterpret_cast<const u32x4*>(sptr + (i * 4 + GB) * 16);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(aptr + GB * 64);
+    const u32x4 sv = *reinterpret_cast<const u32x4*>(sptr + GB * 16);
     const f32x4 corr_a = mfma_corr(sv, bca);
     f32x4 corr_b = corr_a;
     if constexpr (!SAMEC) corr_b = mfma_corr(sv, bcb);
@@ -198,26 +184,101 @@ __device__ __forceinline__ void dec_mfma_kb(int i, f32x4 (&acc)[NS], const u32x2
       const f32x4 dd = mfma32(a, b, second ? corr_b : corr_a);
       // lane GB*16 + r holds scales (r, GB & 2) and (r, (GB & 2) + 1)
       const uint32_t sw = (uint32_t)__shfl((int)ws[i][j], GB * 16 + r, 64);
-      const float s = f16_to_f32((GB & 1) ? (sw >> 16) : sw);
+      float s = f16_to_f32((GB & 1) ? (sw >> 16) : sw);
+      if constexpr (GUARD) s = live ? s : 0.f;
 #pragma unroll
       for (int m = 0; m < MR; ++m) acc[j][m] = fmaf(s, dd[m], acc[j][m]);
     }
   }
 }
 
-// Tile loads run PRE k-blocks ahead of the matrix-core work, in the wave's
-// own instruction stream: when the memory system pushes back on issue, the
-// wave keeps computing on the tiles it already has.  On entry the loads of
-// k-blocks 0 .. PRE-1 are issued and the copies into LDS have landed.
-template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, int MR>
-__device__ __forceinline__ void dec_pipeline(f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS],
-                                             uint32_t (&wh)[KBW][NS], uint32_t (&ws)[KBW][NS],
-                                             const uint8_t* const (&code_base)[2],
-                                             const size_t (&plane1)[2],
-                                             const size_t (&scale_off)[2], const int (&nt)[NS],
-                                             int KB, int kb0, int nkb, int lane,
-                                             const uint8_t* aptr, const uint8_t* sptr, u32x4 bca,
-                                             u32x4 bcb, const Unpack2R& ur) {
+// 4. A wave's k-blocks: k-block i's rows, sums and tiles are fetched PRE
+//    k-blocks ahead of its matrix-core work, in the wave's own instruction
+//    stream (when the memory system pushes back on issue, the wave keeps
+//    computing on what it has); its rows and sums are written to the wave's
+//    LDS buffer just before its turn (LDS operations of a wave run in order,
+//    so the writes wait for the previous k-block's reads).  With FULL the
+//    wave owns KBW k-blocks, otherwise those past nkb add zero.
+template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, int MR, int RC,
+          bool FULL>
+__device__ __forceinline__ void dec_pipeline(
+    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], uint32_t (&ws)[KBW][NS],
+    const uint8_t* const (&code_base)[2], const size_t (&plane1)[2], const size_t (&scale_off)[2],
+    const int (&nt)[NS], int KB, int kb0, int nkb, int lane, uint8_t* buf, int M, bool gather,
+    int row0, uint32_t tok3, const uint16_t* __restrict__ A, const uint8_t* __restrict__ Asum,
+    int K, u32x4 bca, u32x4 bcb, const Unpack2R& ur) {
+  const int q = lane >> 4, r = lane & 15;
+  const int arow = r < M ? r : 0;
+  KbRegs<RC> v[KBW];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    dec_kb_fetch<RC>(v[i], lane, M, gather, row0, tok3, A, Asum, K, min(kb0 + i, KB - 1));
+    dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
+                                           kb0, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    if (i + PRE < KBW) {
+      dec_kb_fetch<RC>(v[i + PRE], lane, M, gather, row0, tok3, A, Asum, K,
+                       min(kb0 + i + PRE, KB - 1));
+      dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i + PRE, wc, wh, ws, code_base, plane1, scale_off,
+                                             nt, KB, kb0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dec_kb_store<RC, !GATEUP>(buf, v[i], lane);
+    dec_mfma_kb<NS, GATEUP, QA3, QB3, SAMEC, KBW, MR, !FULL>(
+        i, acc, wc, wh, ws, buf + arow * ring_row_stride() + q * 16,
+        buf + RC * ring_row_stride() + arow * 64, bca, bcb, ur, r, i < nkb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// 4'. The same for a single-token launch: the wave's whole slice of the row
+//     (KBW k-blocks, [KBW][256 B], then the sums [KBW][64 B]) is fetched into
+//     registers ahead of the first tiles and written to LDS once; a k-block's
+//     work then only reads LDS.  Lanes read the same row: LDS broadcasts.
+__host__ __device__ constexpr int one_wave_bytes(int kbw) { return kbw * (256 + 64); }
+
+template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, bool FULL>
+__device__ __forceinline__ void dec_pipeline_one(
+    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], uint32_t (&ws)[KBW][NS],
+    const uint8_t* const (&code_base)[2], const size_t (&plane1)[2], const size_t (&scale_off)[2],
+    const int (&nt)[NS], int KB, int kb0, int nkb, int lane, uint8_t* buf, bool gather, int row0,
+    uint32_t tok3, const uint16_t* __restrict__ A, const uint8_t* __restrict__ Asum, int K,
+    u32x4 bca, u32x4 bcb, const Unpack2R& ur) {
+  constexpr int NPA = (KBW * 16 + 63) / 64;  // 16-byte pieces of the slice per lane
+  const int G = K / 32;
+  const int src = dec_src_row(0, gather, row0, tok3);
+  const uint8_t* arow = reinterpret_cast<const uint8_t*>(A + (size_t)src * K);
+  u32x4 va[NPA];
+#pragma unroll
+  for (int p = 0; p < NPA; ++p) {
+    const int piece = (p * 64 + lane) & (KBW * 16 - 1);
+    const int kb = min(kb0 + (piece >> 4), KB - 1);
+    va[p] = *reinterpret_cast<const u32x4*>(arow + kb * 256 + (piece & 15) * 16);
+  }
+  const int spiece = lane & (KBW * 4 - 1);
+  u32x4 vs = *reinterpret_cast<const u32x4*>(
+      Asum + (size_t)src * G * 16 + (min(kb0 + (spiece >> 2), KB - 1) * 4 + (spiece & 3)) * 16);
+#pragma unroll
+  for (int i = 0; i < PRE; ++i)
+    dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
+                                           kb0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < NPA; ++p) {
+    const int piece = (p * 64 + lane) & (KBW * 16 - 1);
+    *reinterpret_cast<u32x4*>(buf + piece * 16) = va[p];
+  }
+  if constexpr (!GATEUP) {
+    // (Wa, Sa, Wb, Sb): fp32 sums of h over the group's two 16-column halves
+    const uint4 st = stage_sums(__uint_as_float(vs[0]) + __uint_as_float(vs[2]),
+                                __uint_as_float(vs[1]) + __uint_as_float(vs[3]));
+    vs = u32x4{st.x, st.y, st.z, st.w};
+  }
+  *reinterpret_cast<u32x4*>(buf + KBW * 256 + spiece * 16) = vs;
+  const int q = lane >> 4;
 #pragma unroll
   for (int i = 0; i < KBW; ++i) {
     if (i + PRE < KBW) {
@@ -225,9 +286,9 @@ __device__ __forceinline__ void dec_pipeline(f32x4 (&acc)[NS], u32x2 (&wc)[KBW][
                                              nt, KB, kb0, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (i < nkb)
-      dec_mfma_kb<NS, GATEUP, QA3, QB3, SAMEC, KBW, MR>(i, acc, wc, wh, ws, aptr, sptr, bca, bcb,
-                                                        ur, lane & 15);
+    dec_mfma_kb<NS, GATEUP, QA3, QB3, SAMEC, KBW, 1, !FULL>(
+        i, acc, wc, wh, ws, buf + i * 256 + q * 16, buf + KBW * 256 + i * 64, bca, bcb, ur,
+        lane & 15, i < nkb);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -239,13 +300,16 @@ __device__ __forceinline__ void dec_pipeline(f32x4 (&acc)[NS], u32x2 (&wc)[KBW][
 // wave, 2 for 16).
 __host__ __device__ constexpr int dec_pre(int kbw) { return kbw >= 16 ? 2 : 1; }
 
+
+
 // ------------------------------------------------------- projection kernel
 // GATEUP = true: streams 0 (gate) and 1 (up) of n-tile blockIdx % groups;
 //   epilogue h = bf16(SiLU(g) * u), stored as h/16, plus fp32 (W, S) sums of
 //   h over the tile's 16 columns (half of a 32-group of the down projection).
 // GATEUP = false (down): streams 0..3 = n-tiles 4g .. 4g+3; the 32-group sums
 //   of h are the two half sums added; epilogue y = bf16(acc).
-// ONE_ROW: launched for a single token, so every slot has M == 1.
+// ONE_ROW: launched for a single token, so every slot has M == 1 (the wave's
+// whole slice of the row is staged at once).
 template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KSPLIT, int KBW, bool ONE_ROW>
 __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
@@ -273,47 +337,49 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
   const uint8_t* const code_base[2] = {blob + pa.off, blob + pb.off};
   const size_t plane1[2] = {pa.plane1, pb.plane1};
   const size_t scale_off[2] = {pa.scales, pb.scales};
-  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = K / 128;
   const int per = (KB + KSPLIT - 1) / KSPLIT;
   const int kb0 = min(KB, wave * per);
   const int nkb = min(KB, kb0 + per) - kb0;  // 0 .. KBW
-  uint8_t* sA = lds + wave * dw_bytes(Mmax, KBW);
-  uint8_t* sS = sA + dw_rows_bytes(Mmax, KBW);
-
-  dec_stage_rows<KBW>(sA, sS, lane, M, GATEUP, row0, tok3, A, Asum, K, kb0, nkb);
-  __builtin_amdgcn_sched_barrier(0);
   int nt[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) nt[j] = GATEUP ? grp : grp * 4 + j;
   constexpr int PRE = dec_pre(KBW);
-  u32x2 wc[KBW][NS];
-  uint32_t wh[KBW][NS], ws[KBW][NS];
-#pragma unroll
-  for (int i = 0; i < PRE; ++i)
-    dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
-                                           kb0, lane);
-  wait_for_copies<PRE * dec_kb_loads<NS, GATEUP, QA3, QB3>()>();
-  if constexpr (!GATEUP) dec_half_sums_to_staged<KBW>(sS, lane, M, nkb);
-
   const u32x4 bca = corr_b_operand(q == 0, QA3, ca);
   const u32x4 bcb = corr_b_operand(q == 0, QB3, cb);
   const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1), lane_copy(uk.b2)};
-  const int arow = r < M ? r : 0;
-  const uint8_t* aptr = sA + arow * dw_row_stride(KBW) + q * 16;
-  const uint8_t* sptr = sS + arow * KBW * 64;
   f32x4 acc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (ONE_ROW || M == 1)
-    dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 1>(acc, wc, wh, ws, code_base, plane1,
-                                                           scale_off, nt, KB, kb0, nkb, lane,
-                                                           aptr, sptr, bca, bcb, ur);
-  else
-    dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 4>(acc, wc, wh, ws, code_base, plane1,
-                                                           scale_off, nt, KB, kb0, nkb, lane,
-                                                           aptr, sptr, bca, bcb, ur);
+  u32x2 wc[KBW][NS];
+  uint32_t wh[KBW][NS], ws[KBW][NS];
+  if constexpr (ONE_ROW) {
+    uint8_t* buf = lds + wave * one_wave_bytes(KBW);
+    if (nkb < KBW)
+      dec_pipeline_one<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, false>(
+          acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, GATEUP,
+          row0, tok3, A, Asum, K, bca, bcb, ur);
+    else
+      dec_pipeline_one<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, true>(
+          acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, GATEUP,
+          row0, tok3, A, Asum, K, bca, bcb, ur);
+  } else {
+    uint8_t* buf = lds + wave * ring_wave_bytes(kDecMaxRows);
+    if (nkb < KBW)
+      dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 4, kDecMaxRows, false>(
+          acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
+          row0, tok3, A, Asum, K, bca, bcb, ur);
+    else if (M == 1)
+      dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 1, 1, true>(
+          acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
+          row0, tok3, A, Asum, K, bca, bcb, ur);
+    else
+      dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 4, kDecMaxRows, true>(
+          acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
+          row0, tok3, A, Asum, K, bca, bcb, ur);
+  }
 
   // 5. cross-wave reduction in a fixed order (every wave is done with LDS)
   __syncthreads();
@@ -384,7 +450,8 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = blockIdx.x;
   const int rows_total = T * k + T * n_shared;
-  float* ylds = reinterpret_cast<float*>(lds + nwaves * dw_bytes(Mmax, KBW));  // [rows][16]
+  constexpr int WB = ONE_ROW ? one_wave_bytes(KBW) : ring_wave_bytes(kDecMaxRows);
+  float* ylds = reinterpret_cast<float*>(lds + nwaves * WB);  // [rows][16]
   int* s_inv = reinterpret_cast<int*>(ylds + rows_total * 16);
   float* s_w = reinterpret_cast<float*>(s_inv + kDecodeMaxRoutedRows);
   // the combine's inputs, loaded first (they are long complete when used)
@@ -403,35 +470,38 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
     const size_t plane1[2] = {pd.plane1, pd.plane1};
     const size_t scale_off[2] = {pd.scales, pd.scales};
     const int KB = K / 128;
-    uint8_t* sA = lds + wave * dw_bytes(Mmax, KBW);
-    uint8_t* sS = sA + dw_rows_bytes(Mmax, KBW);
-    dec_stage_rows<KBW>(sA, sS, lane, M, false, row0, 0u, hs, hsum, K, 0, KB);
-    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* buf = lds + wave * WB;
     const int ntl[1] = {nt};
     constexpr int PRE = dec_pre(KBW);
     u32x2 wc[KBW][1];
     uint32_t wh[KBW][1], ws[KBW][1];
-#pragma unroll
-    for (int i = 0; i < PRE; ++i)
-      dec_load_kb<1, false, Q3, Q3, KBW>(i, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0,
-                                         lane);
-    wait_for_copies<PRE * dec_kb_loads<1, false, Q3, Q3>()>();
-    dec_half_sums_to_staged<KBW>(sS, lane, M, KB);
     const u32x4 bc = corr_b_operand(q == 0, Q3, cd);
     const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1),
                          lane_copy(uk.b2)};
-    const int arow = r < M ? r : 0;
-    const uint8_t* aptr = sA + arow * dw_row_stride(KBW) + q * 16;
-    const uint8_t* sptr = sS + arow * KBW * 64;
     f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (ONE_ROW || M == 1)
-      dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 1>(acc, wc, wh, ws, code_base, plane1,
-                                                        scale_off, ntl, KB, 0, KB, lane, aptr,
-                                                        sptr, bc, bc, ur);
-    else
-      dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 4>(acc, wc, wh, ws, code_base, plane1,
-                                                        scale_off, ntl, KB, 0, KB, lane, aptr,
-                                                        sptr, bc, bc, ur);
+    if constexpr (ONE_ROW) {
+      if (KB < KBW)
+        dec_pipeline_one<1, false, Q3, Q3, true, KBW, PRE, false>(
+            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, false, row0,
+            0u, hs, hsum, K, bc, bc, ur);
+      else
+        dec_pipeline_one<1, false, Q3, Q3, true, KBW, PRE, true>(
+            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, false, row0,
+            0u, hs, hsum, K, bc, bc, ur);
+    } else {
+      if (KB < KBW)
+        dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 4, kDecMaxRows, false>(
+            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
+            row0, 0u, hs, hsum, K, bc, bc, ur);
+      else if (M == 1)
+        dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 1, 1, true>(
+            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
+            row0, 0u, hs, hsum, K, bc, bc, ur);
+      else
+        dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 4, kDecMaxRows, true>(
+            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
+            row0, 0u, hs, hsum, K, bc, bc, ur);
+    }
     // rows 4*(lane/16) + i, column lane % 16 -> y of permuted row row0 + row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -493,7 +563,8 @@ static DecShape dec_shape(bool gateup, int K) {
 }
 
 static size_t dec_lds_bytes(bool gateup, DecShape sh, int Mmax) {
-  const size_t rows = (size_t)sh.ksplit * dw_bytes(Mmax, sh.kbw);
+  const size_t rows =
+      (size_t)sh.ksplit * (Mmax == 1 ? one_wave_bytes(sh.kbw) : ring_wave_bytes(kDecMaxRows));
   const size_t red = (size_t)sh.ksplit * (gateup ? 2 : 4) * 4 * 32 * 4;
   return rows > red ? rows : red;
 }
@@ -524,7 +595,9 @@ static int dc_kbw(int I) {
 static size_t dc_lds_bytes(const moe_layer* L, int T, int max_slots, int Mmax) {
   const int waves = dc_waves(T, max_slots);
   const int rows = T * L->top_k + T * L->n_shared;
-  return (size_t)waves * dw_bytes(Mmax, dc_kbw(L->inter)) + (size_t)rows * 16 * 4 +
+  const int kbw = dc_kbw(L->inter);
+  return (size_t)waves * (Mmax == 1 ? one_wave_bytes(kbw) : ring_wave_bytes(kDecMaxRows)) +
+         (size_t)rows * 16 * 4 +
          (size_t)kDecodeMaxRoutedRows * 8;
 }
 

@@ -1,13 +1,13 @@
 """Static checks of the decode kernels' generated gfx950 code (no GPU needed).
 
-Each decode wave copies its activation slice into LDS with direct-to-LDS
-loads, then issues a fixed number of packed-tile loads, then waits with
-`s_waitcnt vmcnt(N)` until only those N loads can be outstanding: loads
-complete in issue order, so the copies have landed.  That is only right if
-exactly N vector-memory loads sit between the last copy and the wait, which
-depends on the compiler keeping one instruction per tile load in that order.
-These tests compile the kernels to assembly and check it, along with the
-absence of register spills.
+A decode wave fetches each k-block's activation rows, their sums and its
+packed tiles into registers one k-block ahead of the matrix-core work, and
+writes the rows through a small LDS buffer just before their use.  All of its
+waits are placed by the compiler.  Two ways the compiler can quietly undo the
+prefetch are checked here: a full `s_waitcnt vmcnt(0)` ahead of loads issued
+later in the same straight-line block (the stream drains at every k-block),
+and direct-to-LDS loads (whose hazard tracking forces such drains).  Also
+checked: no register spills.
 """
 import os
 import re
@@ -39,27 +39,32 @@ def _functions(text, prefix):
     return funcs
 
 
-def test_tile_loads_match_the_copy_wait(asm):
+def _blocks(body):
+    """Straight-line pieces of a function: split at labels and branches."""
+    block = []
+    for line in body.splitlines():
+        l = line.strip()
+        if l.startswith(".LBB") or l.startswith("s_cbranch") or l.startswith("s_branch"):
+            if block:
+                yield block
+            block = []
+        elif l and not l.startswith(";"):
+            block.append(l)
+    if block:
+        yield block
+
+
+def test_no_drain_ahead_of_later_loads(asm):
     funcs = _functions(asm, "_ZN5bqmoe10k_dec_proj")
     funcs.update(_functions(asm, "_ZN5bqmoe18k_dec_down_combine"))
     assert len(funcs) >= 30
     for name, body in funcs.items():
-        lines = [l.strip() for l in body.splitlines()]
-        lds = [i for i, l in enumerate(lines) if l.startswith("global_load_lds")]
-        assert lds, name
-        last = max(lds)
-        wait = next(i for i in range(last, len(lines)) if l_wait(lines[i]) is not None)
-        n = l_wait(lines[wait])
-        loads = [l for l in lines[last + 1:wait] if re.match(r"global_load_(?!lds)", l)]
-        assert len(loads) == n, (name, len(loads), n)
-        # nothing but tile loads between the copies and the wait touches memory
-        assert not any(re.match(r"(global|buffer|flat)_(store|atomic)", l)
-                       for l in lines[last + 1:wait]), name
-
-
-def l_wait(line):
-    m = re.match(r"s_waitcnt vmcnt\((\d+)\)", line)
-    return int(m.group(1)) if m else None
+        assert "global_load_lds" not in body, name
+        for block in _blocks(body):
+            loads = [i for i, l in enumerate(block) if re.match(r"global_load", l)]
+            drains = [i for i, l in enumerate(block) if re.match(r"s_waitcnt vmcnt\(0\)", l)]
+            if loads and drains:
+                assert min(drains) > max(loads), (name, block[min(drains) - 3:min(drains) + 3])
 
 
 def test_no_scratch(asm):
