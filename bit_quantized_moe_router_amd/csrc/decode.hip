@@ -70,7 +70,7 @@ struct KbRegs {
   u32x4 s;                       // one 32-group of one row (lanes < 4 RC)
 };
 
-template <int RC>
+template <int RC, bool CLAMP>
 __device__ __forceinline__ void dec_kb_fetch(KbRegs<RC>& v, int lane, int M, bool gather,
                                              int base, uint32_t tok3,
                                              const uint16_t* __restrict__ A,
@@ -113,26 +113,27 @@ __device__ __forceinline__ void dec_kb_store(uint8_t* buf, const KbRegs<RC>& v, 
 }
 
 // 2. Packed tiles of one of a wave's k-blocks (kb0 + i) for NS streams: codes
-//    (8 B / lane), level bit 2 (4 B / lane, 3-bit only), scales of row r,
-//    groups q & 2 and (q & 2) + 1 (4 B / lane).  Stream j reads n-tile nt[j]
-//    of projection second(j) = (GATEUP && j == 1).  The loads are
-//    unconditional (a wave past the last k-block re-reads the last tile), so
-//    that their number per k-block is the compile-time constant
-//    dec_kb_loads().
+//    (8 B / lane), level bit 2 (4 B / lane, 3-bit only), and the 4 group
+//    scales of the lane's column r (8 B / lane; the 4 lanes of a column read
+//    the same bytes).  Stream j reads n-tile nt[j] of projection second(j) =
+//    (GATEUP && j == 1).  The loads are unconditional; with CLAMP a wave past
+//    the last k-block re-reads the last tile, without it (a wave that owns
+//    all KBW k-blocks) the addresses of successive k-blocks differ by
+//    constants.
 template <int NS, bool GATEUP, bool QA3, bool QB3>
 __host__ __device__ constexpr int dec_kb_loads() {
   return (2 + (QA3 ? 1 : 0)) + (NS - 1) * (2 + ((GATEUP ? QB3 : QA3) ? 1 : 0));
 }
 
-template <int NS, bool GATEUP, bool QA3, bool QB3, int KBW>
+template <int NS, bool GATEUP, bool QA3, bool QB3, int KBW, bool CLAMP>
 __device__ __forceinline__ void dec_load_kb(int i, u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS],
-                                            uint32_t (&ws)[KBW][NS],
+                                            u32x2 (&ws)[KBW][NS],
                                             const uint8_t* const (&code_base)[2],
                                             const size_t (&plane1)[2],
                                             const size_t (&scale_off)[2], const int (&nt)[NS],
                                             int KB, int kb0, int lane) {
-  const int q = lane >> 4, r = lane & 15;
-  const int kbc = min(kb0 + i, KB - 1);
+  const int r = lane & 15;
+  const int kbc = CLAMP ? min(kb0 + i, KB - 1) : kb0 + i;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int second = GATEUP && j == 1;
@@ -143,8 +144,7 @@ __device__ __forceinline__ void dec_load_kb(int i, u32x2 (&wc)[KBW][NS], uint32_
     wh[i][j] =
         q3 ? *reinterpret_cast<const uint32_t*>(base + plane1[second] + tile * 256 + lane * 4)
            : 0u;
-    ws[i][j] = *reinterpret_cast<const uint32_t*>(base + scale_off[second] + tile * 128 +
-                                                  (r * 4 + (q & 2)) * 2);
+    ws[i][j] = *reinterpret_cast<const u32x2*>(base + scale_off[second] + tile * 128 + r * 8);
   }
 }
 
@@ -157,9 +157,9 @@ __device__ __forceinline__ void dec_load_kb(int i, u32x2 (&wc)[KBW][NS], uint32_
 template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int MR, bool GUARD>
 __device__ __forceinline__ void dec_mfma_kb(int i, f32x4 (&acc)[NS], const u32x2 (&wc)[KBW][NS],
                                             const uint32_t (&wh)[KBW][NS],
-                                            const uint32_t (&ws)[KBW][NS], const uint8_t* aptr,
+                                            const u32x2 (&ws)[KBW][NS], const uint8_t* aptr,
                                             const uint8_t* sptr, u32x4 bca, u32x4 bcb,
-                                            const Unpack2R& ur, int r, bool live = true) {
+                                            const Unpack2R& ur, bool live = true) {
 #pragma unroll
   for (int GB = 0; GB < 4; ++GB) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(aptr + GB * 64);
@@ -182,8 +182,8 @@ __device__ __forceinline__ void dec_mfma_kb(int i, f32x4 (&acc)[NS], const u32x2
         b = (GB & 1) ? unpack2_r<1>(word, ur) : unpack2_r<0>(word, ur);
       }
       const f32x4 dd = mfma32(a, b, second ? corr_b : corr_a);
-      // lane GB*16 + r holds scales (r, GB & 2) and (r, (GB & 2) + 1)
-      const uint32_t sw = (uint32_t)__shfl((int)ws[i][j], GB * 16 + r, 64);
+      // fp16 scale of (column r, group GB): half GB & 1 of word GB >> 1
+      const uint32_t sw = ws[i][j][GB >> 1];
       float s = f16_to_f32((GB & 1) ? (sw >> 16) : sw);
       if constexpr (GUARD) s = live ? s : 0.f;
 #pragma unroll
@@ -202,7 +202,7 @@ __device__ __forceinline__ void dec_mfma_kb(int i, f32x4 (&acc)[NS], const u32x2
 template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, int MR, int RC,
           bool FULL>
 __device__ __forceinline__ void dec_pipeline(
-    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], uint32_t (&ws)[KBW][NS],
+    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], u32x2 (&ws)[KBW][NS],
     const uint8_t* const (&code_base)[2], const size_t (&plane1)[2], const size_t (&scale_off)[2],
     const int (&nt)[NS], int KB, int kb0, int nkb, int lane, uint8_t* buf, int M, bool gather,
     int row0, uint32_t tok3, const uint16_t* __restrict__ A, const uint8_t* __restrict__ Asum,
@@ -212,24 +212,25 @@ __device__ __forceinline__ void dec_pipeline(
   KbRegs<RC> v[KBW];
 #pragma unroll
   for (int i = 0; i < PRE; ++i) {
-    dec_kb_fetch<RC>(v[i], lane, M, gather, row0, tok3, A, Asum, K, min(kb0 + i, KB - 1));
-    dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
+    dec_kb_fetch<RC, !FULL>(v[i], lane, M, gather, row0, tok3, A, Asum, K,
+                            FULL ? kb0 + i : min(kb0 + i, KB - 1));
+    dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
                                            kb0, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < KBW; ++i) {
     if (i + PRE < KBW) {
-      dec_kb_fetch<RC>(v[i + PRE], lane, M, gather, row0, tok3, A, Asum, K,
-                       min(kb0 + i + PRE, KB - 1));
-      dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i + PRE, wc, wh, ws, code_base, plane1, scale_off,
+      dec_kb_fetch<RC, !FULL>(v[i + PRE], lane, M, gather, row0, tok3, A, Asum, K,
+                              FULL ? kb0 + i + PRE : min(kb0 + i + PRE, KB - 1));
+      dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i + PRE, wc, wh, ws, code_base, plane1, scale_off,
                                              nt, KB, kb0, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     dec_kb_store<RC, !GATEUP>(buf, v[i], lane);
     dec_mfma_kb<NS, GATEUP, QA3, QB3, SAMEC, KBW, MR, !FULL>(
         i, acc, wc, wh, ws, buf + arow * ring_row_stride() + q * 16,
-        buf + RC * ring_row_stride() + arow * 64, bca, bcb, ur, r, i < nkb);
+        buf + RC * ring_row_stride() + arow * 64, bca, bcb, ur, i < nkb);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -242,7 +243,7 @@ __host__ __device__ constexpr int one_wave_bytes(int kbw) { return kbw * (256 + 
 
 template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, bool FULL>
 __device__ __forceinline__ void dec_pipeline_one(
-    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], uint32_t (&ws)[KBW][NS],
+    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], u32x2 (&ws)[KBW][NS],
     const uint8_t* const (&code_base)[2], const size_t (&plane1)[2], const size_t (&scale_off)[2],
     const int (&nt)[NS], int KB, int kb0, int nkb, int lane, uint8_t* buf, bool gather, int row0,
     uint32_t tok3, const uint16_t* __restrict__ A, const uint8_t* __restrict__ Asum, int K,
@@ -255,15 +256,16 @@ __device__ __forceinline__ void dec_pipeline_one(
 #pragma unroll
   for (int p = 0; p < NPA; ++p) {
     const int piece = (p * 64 + lane) & (KBW * 16 - 1);
-    const int kb = min(kb0 + (piece >> 4), KB - 1);
+    const int kb = FULL ? kb0 + (piece >> 4) : min(kb0 + (piece >> 4), KB - 1);
     va[p] = *reinterpret_cast<const u32x4*>(arow + kb * 256 + (piece & 15) * 16);
   }
   const int spiece = lane & (KBW * 4 - 1);
   u32x4 vs = *reinterpret_cast<const u32x4*>(
-      Asum + (size_t)src * G * 16 + (min(kb0 + (spiece >> 2), KB - 1) * 4 + (spiece & 3)) * 16);
+      Asum + (size_t)src * G * 16 +
+      ((FULL ? kb0 + (spiece >> 2) : min(kb0 + (spiece >> 2), KB - 1)) * 4 + (spiece & 3)) * 16);
 #pragma unroll
   for (int i = 0; i < PRE; ++i)
-    dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
+    dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
                                            kb0, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -282,13 +284,13 @@ __device__ __forceinline__ void dec_pipeline_one(
 #pragma unroll
   for (int i = 0; i < KBW; ++i) {
     if (i + PRE < KBW) {
-      dec_load_kb<NS, GATEUP, QA3, QB3, KBW>(i + PRE, wc, wh, ws, code_base, plane1, scale_off,
+      dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i + PRE, wc, wh, ws, code_base, plane1, scale_off,
                                              nt, KB, kb0, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     dec_mfma_kb<NS, GATEUP, QA3, QB3, SAMEC, KBW, 1, !FULL>(
         i, acc, wc, wh, ws, buf + i * 256 + q * 16, buf + KBW * 256 + i * 64, bca, bcb, ur,
-        lane & 15, i < nkb);
+        i < nkb);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -354,7 +356,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x2 wc[KBW][NS];
-  uint32_t wh[KBW][NS], ws[KBW][NS];
+  uint32_t wh[KBW][NS];
+  u32x2 ws[KBW][NS];
   if constexpr (ONE_ROW) {
     uint8_t* buf = lds + wave * one_wave_bytes(KBW);
     if (nkb < KBW)
@@ -474,7 +477,8 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
     const int ntl[1] = {nt};
     constexpr int PRE = dec_pre(KBW);
     u32x2 wc[KBW][1];
-    uint32_t wh[KBW][1], ws[KBW][1];
+    uint32_t wh[KBW][1];
+    u32x2 ws[KBW][1];
     const u32x4 bc = corr_b_operand(q == 0, Q3, cd);
     const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1),
                          lane_copy(uk.b2)};
@@ -551,10 +555,14 @@ struct DecShape {
   int ksplit, kbw;
 };
 
-static DecShape dec_shape(bool gateup, int K) {
-  const int KB = K / 128, cap = gateup ? 8 : 4;
+// Down launches for a single token split K over up to 16 waves of at most 4
+// k-blocks; for several rows at most 8 waves of up to 8 k-blocks (a 16-wave
+// block leaves 128 registers per lane, too few for 8 rows of 4 streams).
+static DecShape dec_shape(bool gateup, int K, int Mmax) {
+  const int KB = K / 128;
+  const int cap = gateup || Mmax > 1 ? 8 : 4, kmax = gateup || Mmax > 1 ? 8 : 16;
   int ks = 4;
-  while (ks < (gateup ? 8 : 16) && (KB + ks - 1) / ks > cap) ks *= 2;
+  while (ks < kmax && (KB + ks - 1) / ks > cap) ks *= 2;
   const int per = (KB + ks - 1) / ks;
   if (per > cap) return {0, 0};
   int kbw = 2;
@@ -573,7 +581,7 @@ constexpr size_t kLdsLimit = 160 * 1024;
 
 bool decode_shape_ok(const moe_layer* L, int T) {
   const int Mmax = T < kDecMaxRows ? T : kDecMaxRows;
-  const DecShape gu = dec_shape(true, L->d), dn = dec_shape(false, L->inter);
+  const DecShape gu = dec_shape(true, L->d, Mmax), dn = dec_shape(false, L->inter, Mmax);
   return gu.ksplit && dn.ksplit && dec_lds_bytes(true, gu, Mmax) <= kLdsLimit &&
          dec_lds_bytes(false, dn, Mmax) <= kLdsLimit;
 }
@@ -618,11 +626,13 @@ static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const
                          dim3(64 * KS), lds, s, (const uint8_t*)L->experts, L->expert_stride, \
                          (const uint8_t*)L->shared, pa, pb, slots, A, Asum, K, N, Mmax, ca,   \
                          cb, out, psum, kUnpack2);                                            \
-    else                                                                                      \
+    else if constexpr (KS < 16)                                                               \
       hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, false>),               \
                          dim3(n_blocks), dim3(64 * KS), lds, s, (const uint8_t*)L->experts,   \
                          L->expert_stride, (const uint8_t*)L->shared, pa, pb, slots, A, Asum, \
                          K, N, Mmax, ca, cb, out, psum, kUnpack2);                            \
+    else                                                                                      \
+      return -1;                                                                              \
   } while (0)
   if (sh.ksplit == 4 && sh.kbw == 2)
     BQ_L(4, 2);
@@ -640,6 +650,8 @@ static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const
       BQ_L(8, 4);
     else if (sh.ksplit == 16 && sh.kbw == 4)
       BQ_L(16, 4);
+    else if (sh.ksplit == 8 && sh.kbw == 8)
+      BQ_L(8, 8);
     else
       return -1;
   }
@@ -662,7 +674,7 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
   uint16_t* y = (uint16_t*)(ws + W.y);
   if (mask & MOE_DECODE_STAGE_GATEUP) {
     const ProjDesc pg = proj(L, 0), pu = proj(L, 1);
-    const DecShape sh = dec_shape(true, d);
+    const DecShape sh = dec_shape(true, d, Mmax);
     const int nb = W.max_slots * (I / 16);
     const float cg = qtype_offset(L->q_gate), cu = qtype_offset(L->q_up);
     const bool g3 = L->q_gate == MOE_Q_INT3, u3 = L->q_up == MOE_Q_INT3;
@@ -724,7 +736,7 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
 #undef BQ_DC
   } else if (mask & MOE_DECODE_STAGE_DOWN) {
     const ProjDesc pd = proj(L, 2);
-    const DecShape sh = dec_shape(false, I);
+    const DecShape sh = dec_shape(false, I, Mmax);
     const int nb = W.max_slots * (d / 64);
     const float cd = qtype_offset(L->q_down);
     const uint8_t* hsb = (const uint8_t*)hsum;
