@@ -174,10 +174,10 @@ __device__ __forceinline__ void dec_mfma_kb(int i, f32x4 (&acc)[NS], const u32x2
       const uint32_t word = (GB < 2) ? wc[i][j][0] : wc[i][j][1];
       u32x4 b;
       if (q3) {
-        if (GB == 0) b = unpack3<0>(word, wh[i][j]);
-        if (GB == 1) b = unpack3<1>(word, wh[i][j]);
-        if (GB == 2) b = unpack3<2>(word, wh[i][j]);
-        if (GB == 3) b = unpack3<3>(word, wh[i][j]);
+        if (GB == 0) b = unpack3<0>(word, wh[i][j], ur);
+        if (GB == 1) b = unpack3<1>(word, wh[i][j], ur);
+        if (GB == 2) b = unpack3<2>(word, wh[i][j], ur);
+        if (GB == 3) b = unpack3<3>(word, wh[i][j], ur);
       } else {
         b = (GB & 1) ? unpack2_r<1>(word, ur) : unpack2_r<0>(word, ur);
       }
@@ -349,8 +349,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
 #pragma unroll
   for (int j = 0; j < NS; ++j) nt[j] = GATEUP ? grp : grp * 4 + j;
   constexpr int PRE = dec_pre(KBW);
-  const u32x4 bca = corr_b_operand(q == 0, QA3, ca);
-  const u32x4 bcb = corr_b_operand(q == 0, QB3, cb);
+  const u32x4 bca = corr_b_operand(q == 0, ca);
+  const u32x4 bcb = corr_b_operand(q == 0, cb);
   const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1), lane_copy(uk.b2)};
   f32x4 acc[NS];
 #pragma unroll
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
     u32x2 wc[KBW][1];
     uint32_t wh[KBW][1];
     u32x2 ws[KBW][1];
-    const u32x4 bc = corr_b_operand(q == 0, Q3, cd);
+    const u32x4 bc = corr_b_operand(q == 0, cd);
     const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1),
                          lane_copy(uk.b2)};
     f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};

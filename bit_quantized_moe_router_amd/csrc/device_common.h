@@ -86,14 +86,14 @@ __device__ __forceinline__ uint4 stage_sums(float W, float S) {
   return v;
 }
 
-// The B operand of the correction op for a projection: 2-bit formats subtract
-// W + offset * S, 3-bit formats (all slots at base 128) subtract (8 + offset) * S.
-__device__ __forceinline__ u32x4 corr_b_operand(bool lane_active, bool q3, float off) {
+// The B operand of the correction op for a projection: every format (its
+// levels sit on the same per-slot bases) subtracts W + offset * S.
+__device__ __forceinline__ u32x4 corr_b_operand(bool lane_active, float off) {
   u32x4 b = {0u, 0u, 0u, 0u};
   if (lane_active) {
     const uint32_t one = 0x3F80u;
-    const uint32_t c = f32_to_bf16(q3 ? 8.0f + off : off);
-    const uint32_t w = q3 ? 0u : one;
+    const uint32_t c = f32_to_bf16(off);
+    const uint32_t w = one;
     b[0] = w | (w << 16);
     b[1] = w | (c << 16);
     b[2] = c | (c << 16);
@@ -117,24 +117,6 @@ __device__ __forceinline__ float slot_weight(int j) {
 // whose unit in the last place is 16, 4 and 1; v = 3 is shifted down to bits
 // [5:4] under base 128.  So one mask-and-or per pair of levels, plus two
 // shifts per 8 levels.
-template <int S>
-__device__ __forceinline__ uint32_t shl_signed(uint32_t w) {
-  if constexpr (S >= 0)
-    return w << S;
-  else
-    return w >> (-S);
-}
-
-template <int F>
-__device__ __forceinline__ uint32_t lo_field(uint32_t w0) {
-  return shl_signed<4 - 2 * F>(w0) & 0x00300030u;
-}
-// bit 2 of a 3-bit level: plane-1 bit 16h + 4gb + v moved to bit 6 of each half
-template <int HB>
-__device__ __forceinline__ uint32_t hi_field(uint32_t w1) {
-  return shl_signed<6 - HB>(w1) & 0x00400040u;
-}
-
 template <int P>
 __device__ __forceinline__ u32x4 unpack2(uint32_t w) {
   const uint32_t x = P ? (w >> 8) : w;
@@ -143,18 +125,6 @@ __device__ __forceinline__ u32x4 unpack2(uint32_t w) {
   r[1] = (x & 0x000C000Cu) | 0x44004400u;
   r[2] = (x & 0x00300030u) | 0x43004300u;
   r[3] = ((x >> 2) & 0x00300030u) | 0x43004300u;
-  return r;
-}
-
-// 3-bit levels of group GB (0..3 inside the k-block): 128 + 16u, u <= 7.
-template <int GB>
-__device__ __forceinline__ u32x4 unpack3(uint32_t w0, uint32_t w1) {
-  constexpr int P = GB & 1;
-  u32x4 r;
-  r[0] = lo_field<4 * P + 0>(w0) | hi_field<4 * GB + 0>(w1) | 0x43004300u;
-  r[1] = lo_field<4 * P + 1>(w0) | hi_field<4 * GB + 1>(w1) | 0x43004300u;
-  r[2] = lo_field<4 * P + 2>(w0) | hi_field<4 * GB + 2>(w1) | 0x43004300u;
-  r[3] = lo_field<4 * P + 3>(w0) | hi_field<4 * GB + 3>(w1) | 0x43004300u;
   return r;
 }
 
@@ -191,6 +161,33 @@ __device__ __forceinline__ u32x4 unpack2_r(uint32_t w, const Unpack2R& c) {
   r[1] = (x & c.m1) | c.b1;
   r[2] = (x & c.m2) | c.b2;
   r[3] = ((x >> 2) & c.m2) | c.b2;
+  return r;
+}
+
+// 3-bit levels of group GB (0..3 inside the k-block) on the same bases as the
+// 2-bit ones: the level's two low bits stay where unpack2_r leaves them and
+// its bit 2 (from the plane-1 word w1) is inserted just above them, giving
+// base_v + 16u with u <= 7 (bits [2v+2:2v] for v = 0, 1, 2; v = 3 is moved
+// down to v = 2's place, as in unpack2_r).  Plane 1 holds the bit of pair v
+// of group gb at 16h + 2v + 2 + (0, 1, 6, 7)[gb] for v <= 2 and at
+// 16h + (0, 1, 14, 15)[gb] for v = 3, so one shift of w1 lines up pairs 0..2
+// of a group and a second one pair 3: per 8 levels, four mask-and-ors, four
+// bit-field inserts and up to four shifts.
+__device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t from, uint32_t into) {
+  return (from & mask) | (into & ~mask);
+}
+
+template <int GB>
+__device__ __forceinline__ u32x4 unpack3(uint32_t w0, uint32_t w1, const Unpack2R& c) {
+  const uint32_t x = (GB & 1) ? (w0 >> 8) : w0;
+  constexpr int SA = GB == 0 ? 0 : GB == 1 ? 1 : GB == 2 ? 6 : 7;
+  const uint32_t ha = w1 >> SA;
+  const uint32_t hb = GB == 0 ? (w1 << 6) : GB == 1 ? (w1 << 5) : GB == 2 ? (w1 >> 8) : (w1 >> 9);
+  u32x4 r;
+  r[0] = bit_insert(0x00040004u, ha, (x & c.m0) | c.b0);
+  r[1] = bit_insert(0x00100010u, ha, (x & c.m1) | c.b1);
+  r[2] = bit_insert(0x00400040u, ha, (x & c.m2) | c.b2);
+  r[3] = bit_insert(0x00400040u, hb, ((x >> 2) & c.m2) | c.b2);
   return r;
 }
 

@@ -1,4 +1,4 @@
-// Host-side packing of one projection into packed format v1 (see moe.h).
+// Host-side packing of one projection into packed format v2 (see moe.h).
 //
 // The format is laid out for the decode kernels: a 512-B tile holds a 16 (n)
 // x 128 (k) block of 2-bit fields, and lane chunk L = 16q + r of a tile is
@@ -6,6 +6,8 @@
 // k-slots 8q..8q+7 of each 32-wide group.  Inside a lane's 32-bit word the two
 // 16-bit halves carry adjacent k-slots (s even / odd) of the same group, so a
 // single mask-and-or turns a pair of fields into a pair of bf16 operands.
+// Bit 2 of a 3-bit level (plane 1) is placed so that one shift lines up pairs
+// 0..2 of a group just above their low bits and another shift pair 3.
 #include <cstring>
 
 #include "moe_internal.h"
@@ -13,6 +15,12 @@
 namespace bqmoe {
 
 static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Plane-1 bit of pair v (k-slots 2v, 2v+1) of group gb, half h (slot parity).
+static int plane1_bit(int gb, int h, int v) {
+  static const int lo3[4] = {0, 1, 6, 7}, pair3[4] = {0, 1, 14, 15};
+  return 16 * h + (v < 3 ? 2 * v + 2 + lo3[gb] : pair3[gb]);
+}
 
 bool format_shape_ok(int qtype, int64_t K, int64_t N) {
   return qtype_levels(qtype) > 0 && K > 0 && N > 0 && K % 128 == 0 && N % 16 == 0 &&
@@ -78,7 +86,7 @@ extern "C" moe_status moe_pack_weights(int qtype, int64_t K, int64_t N, const ui
             const int half = s & 1, pair = s >> 1;
             const int field = 4 * (gb & 1) + pair;
             w0[gb >> 1] |= (u & 3u) << (16 * half + 2 * field);
-            hi |= (u >> 2) << (16 * half + 4 * gb + pair);
+            hi |= (u >> 2) << plane1_bit(gb, half, pair);
           }
         }
         p0[lane * 2 + 0] = w0[0];

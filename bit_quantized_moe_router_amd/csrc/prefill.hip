@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
 
   const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1), lane_copy(uk.b2)};
   // correction B operand: k-slots 0..7 (lanes 0..31) carry the constants
-  const u32x4 bc0 = corr_b_operand(lane < 32, Q3A, ca);
-  const u32x4 bc1 = corr_b_operand(lane < 32, Q3B, cb);
+  const u32x4 bc0 = corr_b_operand(lane < 32, ca);
+  const u32x4 bc1 = corr_b_operand(lane < 32, cb);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
       _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                           \
         const uint32_t word = (GB < 2) ? cw_[ct][h][0] : cw_[ct][h][1];                        \
         if (q3)                                                                                 \
-          b[ct][h] = unpack3<GB>(word, ch_[ct][h]);                                             \
+          b[ct][h] = unpack3<GB>(word, ch_[ct][h], ur);                                         \
         else                                                                                    \
           b[ct][h] = unpack2_r<GB & 1>(word, ur);                                               \
       }                                                                                         \

@@ -71,14 +71,16 @@ enum {
 };
 
 /* ------------------------------------------------------------ packed format
- * Packed format v1 of one projection W[K][N] (K % 128 == 0, N % 16 == 0).
+ * Packed format v2 of one projection W[K][N] (K % 128 == 0, N % 16 == 0).
  * NT = N/16 n-tiles, KB = K/128 k-blocks.  For code (n, k): r = n%16,
  * kk = k%128, gb = kk/32, j = kk%32, q = j/8, s = j%8, lane chunk L = 16q + r.
  *   plane 0 (level & 3): tile (n/16, k/128) at ((n/16)*KB + k/128)*512 B;
  *     chunk L at L*8 holds two little-endian 32-bit words; the code sits in
  *     word gb/2 at bit 16*(s%2) + 2*(4*(gb%2) + s/2).
  *   plane 1 (3-bit only, level >> 2): from the next 256-B boundary, 256 B
- *     per tile, chunk L is one 32-bit word at L*4, bit 16*(s%2) + 4*gb + s/2.
+ *     per tile, chunk L is one 32-bit word at L*4; with v = s/2 the bit is
+ *     16*(s%2) + 2v + 2 + {0,1,6,7}[gb] for v < 3 and 16*(s%2) + {0,1,14,15}[gb]
+ *     for v == 3 (v1 used 16*(s%2) + 4*gb + v).
  *   scales: from the next 256-B boundary, 128 B per (n-tile, k-block) block,
  *     fp16 scale[16*nt + r][4*kb + gb] at index r*4 + gb.
  *   The size is rounded up to a multiple of 256 B.

@@ -40,7 +40,7 @@
  * from the exact double value); logits and weights are fp32; all sums are in
  * double.
  *
- * Packed format v1 (the decoder below; written from the format definition):
+ * Packed format v2 (the decoder below; written from the format definition):
  *   K % 128 == 0 and N % 16 == 0.  NT = N/16 n-tiles, KB = K/128 k-blocks.
  *   plane 0 (u & 3): NT*KB tiles of 512 B, tile (nt,kb) at (nt*KB+kb)*512;
  *     inside, 64 chunks of 8 B (chunk L at L*8) = two little-endian 32-bit
@@ -48,8 +48,8 @@
  *     q = j/8, s = j%8; chunk L = 16q + r; word gb/2; 2-bit field at bit
  *     16*(s%2) + 2*(4*(gb%2) + s/2).
  *   plane 1 (3-bit only, u >> 2): starts at the next 256-B boundary; NT*KB
- *     tiles of 256 B; chunk L (one 32-bit word) at L*4; bit
- *     16*(s%2) + 4*gb + s/2.
+ *     tiles of 256 B; chunk L (one 32-bit word) at L*4; with v = s/2, bit
+ *     16*(s%2) + 2v + 2 + {0,1,6,7}[gb] if v < 3, else 16*(s%2) + {0,1,14,15}[gb].
  *   scales: start at the next 256-B boundary; NT*KB blocks of 128 B; block
  *     (nt,kb) holds fp16 scale s[16nt+r][4kb+gb] at index r*4 + gb.
  *   The blob size is rounded up to a multiple of 256 B.
@@ -163,7 +163,9 @@ int oracle_unpack(int qtype, int64_t K, int64_t N, const uint8_t* blob, size_t b
       unsigned u = (w0 >> bit0) & 3u;
       if (qtype == 3) {
         uint32_t w1 = rd32(blob + p1 + tile * 256 + (size_t)L * 4);
-        int bit1 = (int)(16 * (s % 2) + 4 * gb + s / 2);
+        static const int below3[4] = {0, 1, 6, 7}, third[4] = {0, 1, 14, 15};
+        int v = (int)(s / 2);
+        int bit1 = (int)(16 * (s % 2)) + (v < 3 ? 2 * v + 2 + below3[gb] : third[gb]);
         u |= ((w1 >> bit1) & 1u) << 2;
       }
       if ((int)u >= levels) return -1; /* e.g. level 3 in a ternary matrix */

@@ -31,7 +31,7 @@ double oracle_f16_to_f64(uint16_t h);
 double oracle_code_offset(int qtype);
 int oracle_code_levels(int qtype);
 
-/* Packed format v1: decode a blob back to canonical codes [N][K] and scales [N][K/32]. */
+/* Packed format v2: decode a blob back to canonical codes [N][K] and scales [N][K/32]. */
 size_t oracle_packed_bytes(int qtype, int64_t K, int64_t N);
 int oracle_unpack(int qtype, int64_t K, int64_t N, const uint8_t* blob, size_t blob_bytes,
                   uint8_t* codes, uint16_t* scales);

@@ -1,4 +1,4 @@
-"""Pins for the oracle's decoder of packed format v1.
+"""Pins for the oracle's decoder of packed format v2.
 
 The expected byte/bit positions below were worked out by hand from the format
 definition (see the golden file's notes), not produced by any code here.
@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 
-GOLD = os.path.join(os.path.dirname(__file__), "golden", "format_v1_positions.json")
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "format_v2_positions.json")
 
 
 @pytest.mark.parametrize(
@@ -96,3 +96,15 @@ def test_every_bit_of_plane0_is_one_code():
     blob[: (N // 16) * (K // 128) * 512] = 0xFF
     codes, scales = oracle.unpack(2, K, N, blob)
     assert (codes == 3).all() and not scales.any()
+
+
+def test_every_bit_of_plane1_is_one_code():
+    # The same for the 3-bit plane: with plane 0 all zeros and plane 1 all ones every code is 4,
+    # so each plane-1 bit maps to exactly one (n, k) and all are used.
+    K, N = 256, 32
+    nb = oracle.packed_bytes(3, K, N)
+    tiles = (N // 16) * (K // 128)
+    blob = np.zeros(nb, np.uint8)
+    blob[tiles * 512: tiles * 512 + tiles * 256] = 0xFF
+    codes, scales = oracle.unpack(3, K, N, blob)
+    assert (codes == 4).all() and not scales.any()
