@@ -36,6 +36,7 @@
 
 #include "device_common.h"
 #include "moe_internal.h"
+#include "topk_common.h"
 
 namespace bqmoe {
 
@@ -304,6 +305,101 @@ __host__ __device__ constexpr int dec_pre(int kbw) { return kbw >= 16 ? 2 : 1; }
 
 
 
+// ---------------------------------------- expert selection for one token
+// Outputs of the selection, written by block 0 of a ROUTE launch.
+struct DecRoute {
+  const float* logits;
+  int E, k, n_shared, max_slots;
+  int32_t* ids;
+  float* wts;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_tok;
+  int32_t* inv_row;
+  int32_t* slots;
+};
+
+// Wave 0: top-k of token 0 (wave_topk, E <= 256), the rank of each selected
+// id among them, and this block's slot: (expert, first permuted row, row
+// count), handed to the block's other waves through LDS.  Block 0 also stores
+// the routing outputs, as the select kernel does for T = 1: row j of the
+// token goes to permuted position rank_j.  (The selection repeated by every
+// wave of the launch cost several microseconds of issue.)
+__device__ __forceinline__ void dec_select_one_token(const DecRoute& ro, int slot, int& e,
+                                                     int& row0, int& M) {
+  __shared__ int s_ids[64];
+  __shared__ int s_slot[3];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int k = ro.k;
+  if (tid < 64) {
+    int id;
+    float w;
+    wave_topk<4>(ro.logits, ro.E, k, lane, id, w);
+    int rank = 0;  // selected ids below this lane's (lanes < k)
+    for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(id, j) < id ? 1 : 0;
+    if (lane < k) s_ids[lane] = id;
+    const uint64_t m = __ballot(lane < k && rank == slot);  // whole wave
+    const int e_slot = m ? __builtin_amdgcn_readlane(id, __ffsll((unsigned long long)m) - 1) : -1;
+    if (lane == 0) {
+      if (slot < k) {
+        s_slot[0] = e_slot;
+        s_slot[1] = slot;
+        s_slot[2] = 1;
+      } else {
+        s_slot[0] = -1;
+        s_slot[1] = k;
+        s_slot[2] = slot == k && ro.n_shared ? 1 : 0;
+      }
+    }
+    if (blockIdx.x == 0) {
+      if (lane < k) {
+        ro.ids[lane] = id;
+        ro.wts[lane] = w;
+        ro.inv_row[lane] = rank;
+        ro.perm_tok[lane] = 0;
+        int32_t* rec = ro.slots + kSlotRec * (1 + rank);
+        rec[0] = id;
+        rec[1] = rank;
+        rec[2] = 1;
+        rec[kSlotTok] = 0;
+      }
+      if (lane == 0) {
+        if (ro.n_shared) {
+          int32_t* rec = ro.slots + kSlotRec * (1 + k);
+          rec[0] = -1;
+          rec[1] = k;
+          rec[2] = 1;
+          rec[kSlotTok] = 0;
+        }
+        ro.slots[0] = k + (ro.n_shared ? 1 : 0);
+        ro.offsets[ro.E] = k;
+      }
+    }
+  }
+  __syncthreads();
+  e = __builtin_amdgcn_readfirstlane(s_slot[0]);
+  row0 = __builtin_amdgcn_readfirstlane(s_slot[1]);
+  M = __builtin_amdgcn_readfirstlane(s_slot[2]);
+  if (blockIdx.x != 0) return;
+  for (int x = tid; x < ro.E; x += blockDim.x) {
+    int cnt = 0, off = 0;
+    for (int j = 0; j < k; ++j) {
+      const int o = s_ids[j];
+      cnt += o == x ? 1 : 0;
+      off += o < x ? 1 : 0;
+    }
+    ro.counts[x] = cnt;
+    ro.offsets[x] = off;
+  }
+  // records past the last slot: no rows
+  for (int sidx = k + (ro.n_shared ? 1 : 0) + tid; sidx < ro.max_slots; sidx += blockDim.x) {
+    int32_t* rec = ro.slots + kSlotRec * (1 + sidx);
+    rec[0] = 0;
+    rec[1] = 0;
+    rec[2] = 0;
+  }
+}
+
 // ------------------------------------------------------- projection kernel
 // GATEUP = true: streams 0 (gate) and 1 (up) of n-tile blockIdx % groups;
 //   epilogue h = bf16(SiLU(g) * u), stored as h/16, plus fp32 (W, S) sums of
@@ -312,27 +408,43 @@ __host__ __device__ constexpr int dec_pre(int kbw) { return kbw >= 16 ? 2 : 1; }
 //   of h are the two half sums added; epilogue y = bf16(acc).
 // ONE_ROW: launched for a single token, so every slot has M == 1 (the wave's
 // whole slice of the row is staged at once).
-template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KSPLIT, int KBW, bool ONE_ROW>
+// ROUTE (single-token gate/up, E <= 256): the kernel makes the expert
+// selection itself instead of reading the slot list: wave 0 takes the token's
+// top-k from the logits (the routing kernels' own wave_topk), and the k
+// selected experts in ascending id are slots 0..k-1, then the shared expert
+// (for one token, slot s is also permuted row s).  Block 0 writes every
+// routing output the select kernel would have written (ids, weights, counts,
+// offsets, permutation, slot list), for the down projection and the caller.
+template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KSPLIT, int KBW, bool ONE_ROW,
+          bool ROUTE = false>
 __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ slots, const uint16_t* __restrict__ A,
     const uint8_t* __restrict__ Asum, int K, int N, int Mmax, float ca, float cb,
-    uint16_t* __restrict__ out, float* __restrict__ out_psum, Unpack2K uk) {
+    uint16_t* __restrict__ out, float* __restrict__ out_psum, Unpack2K uk, DecRoute ro) {
   constexpr int NS = GATEUP ? 2 : 4;
+  static_assert(!ROUTE || (GATEUP && ONE_ROW), "selection inside single-token gate/up only");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int groups = N / (16 * (GATEUP ? 1 : 4));
   const int slot = blockIdx.x / groups, grp = blockIdx.x % groups;
-  // the slot record is uniform: scalar loads, which do not wait behind the
-  // packed-tile loads below; records past the last slot have M == 0
-  const int32_t* rec = slots + kSlotRec * (1 + slot);
-  const int e = rec[0], row0 = rec[1], M = rec[2];
-  if (M == 0) return;
+  int e, row0, M;
   uint32_t tok3 = 0;  // tokens of the slot's rows, 3 bits each
-  if (GATEUP) {
+  if constexpr (ROUTE) {
+    dec_select_one_token(ro, slot, e, row0, M);
+  } else {
+    // the slot record is uniform: scalar loads, which do not wait behind the
+    // packed-tile loads below; records past the last slot have M == 0
+    const int32_t* rec = slots + kSlotRec * (1 + slot);
+    e = rec[0];
+    row0 = rec[1];
+    M = rec[2];
+    if (GATEUP) {
 #pragma unroll
-    for (int c = 0; c < kDecMaxRows; ++c)
-      tok3 |= c < M ? (uint32_t)rec[kSlotTok + c] << (3 * c) : 0u;
+      for (int c = 0; c < kDecMaxRows; ++c)
+        tok3 |= c < M ? (uint32_t)rec[kSlotTok + c] << (3 * c) : 0u;
+    }
   }
+  if (M == 0) return;
   const uint8_t* blob = e >= 0 ? experts + (size_t)e * stride : shared;
   // projection offsets in registers before any LDS write (which the compiler
   // cannot tell apart from the argument memory)
@@ -617,20 +729,27 @@ template <bool GATEUP, bool QA3, bool QB3, bool SAMEC>
 static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const moe_layer* L,
                        ProjDesc pa, ProjDesc pb, const int32_t* slots, const uint16_t* A,
                        const uint8_t* Asum, int K, int N, float ca, float cb, uint16_t* out,
-                       float* psum) {
+                       float* psum, const DecRoute* route) {
   const size_t lds = dec_lds_bytes(GATEUP, sh, Mmax);
+  const DecRoute ro = route ? *route : DecRoute{};
 #define BQ_L(KS, KBW)                                                                         \
   do {                                                                                        \
-    if (Mmax == 1)                                                                            \
+    if (Mmax == 1 && route) {                                                                 \
+      if constexpr (GATEUP)                                                                   \
+        hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, true, true>),        \
+                           dim3(n_blocks), dim3(64 * KS), lds, s, (const uint8_t*)L->experts, \
+                           L->expert_stride, (const uint8_t*)L->shared, pa, pb, slots, A,     \
+                           Asum, K, N, Mmax, ca, cb, out, psum, kUnpack2, ro);                \
+    } else if (Mmax == 1)                                                                     \
       hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, true>), dim3(n_blocks), \
                          dim3(64 * KS), lds, s, (const uint8_t*)L->experts, L->expert_stride, \
                          (const uint8_t*)L->shared, pa, pb, slots, A, Asum, K, N, Mmax, ca,   \
-                         cb, out, psum, kUnpack2);                                            \
+                         cb, out, psum, kUnpack2, ro);                                        \
     else if constexpr (KS < 16)                                                               \
       hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, false>),               \
                          dim3(n_blocks), dim3(64 * KS), lds, s, (const uint8_t*)L->experts,   \
                          L->expert_stride, (const uint8_t*)L->shared, pa, pb, slots, A, Asum, \
-                         K, N, Mmax, ca, cb, out, psum, kUnpack2);                            \
+                         K, N, Mmax, ca, cb, out, psum, kUnpack2, ro);                        \
     else                                                                                      \
       return -1;                                                                              \
   } while (0)
@@ -659,9 +778,18 @@ static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const
   return 0;
 }
 
+// Single-token gate/up makes the expert selection itself (see
+// dec_select_one_token) for up to 256 experts; a call that runs the gate/up
+// stage then skips the select kernel.
+static bool select_in_gateup(const moe_layer* L, int T) {
+  return T == 1 && L->n_experts <= 256 && L->top_k <= 64;
+}
+
 int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
                   uint8_t* ws, const DecodeWs& W, uint16_t* out, void* stream, uint32_t mask) {
-  int rc = launch_decode_route(L, x, T, flags, R, ws, W, stream, mask);
+  const bool fused_select = select_in_gateup(L, T) && (mask & MOE_DECODE_STAGE_GATEUP);
+  int rc = launch_decode_route(L, x, T, flags, R, ws, W, stream,
+                               fused_select ? mask & ~(uint32_t)MOE_DECODE_STAGE_SELECT : mask);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const int k = L->top_k, d = L->d, I = L->inter;
@@ -679,9 +807,13 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
     const float cg = qtype_offset(L->q_gate), cu = qtype_offset(L->q_up);
     const bool g3 = L->q_gate == MOE_Q_INT3, u3 = L->q_up == MOE_Q_INT3;
     const bool same = L->q_gate == L->q_up;
+    const DecRoute route = {R->logits,   L->n_experts, k,         L->n_shared, W.max_slots,
+                            R->topk_ids, R->topk_w,    R->counts, R->offsets,  R->perm_tok,
+                            R->inv_row,  (int32_t*)(ws + W.slots)};
+    const DecRoute* rp = fused_select ? &route : nullptr;
 #define BQ_GU(A3, B3, SC)                                                                   \
   rc = launch_proj<true, A3, B3, SC>(sh, nb, Mmax, s, L, pg, pu, slots, xs, xsum, d, I, cg, \
-                                     cu, hs, hsum)
+                                     cu, hs, hsum, rp)
     if (g3 && u3)
       BQ_GU(true, true, true);
     else if (g3)
@@ -742,10 +874,10 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
     const uint8_t* hsb = (const uint8_t*)hsum;
     if (L->q_down == MOE_Q_INT3)
       rc = launch_proj<false, true, true, true>(sh, nb, Mmax, s, L, pd, pd, slots, hs, hsb, I, d,
-                                                cd, cd, y, nullptr);
+                                                cd, cd, y, nullptr, nullptr);
     else
       rc = launch_proj<false, false, false, true>(sh, nb, Mmax, s, L, pd, pd, slots, hs, hsb, I,
-                                                  d, cd, cd, y, nullptr);
+                                                  d, cd, cd, y, nullptr, nullptr);
     if (rc) return rc;
     rc = launch_combine(y, T, d, k, L->n_shared, R->inv_row, R->topk_w, x,
                         (flags & MOE_ADD_RESIDUAL) ? 1 : 0, out, stream);

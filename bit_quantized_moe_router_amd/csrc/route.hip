@@ -10,6 +10,7 @@
 
 #include "device_common.h"
 #include "moe_internal.h"
+#include "topk_common.h"
 
 namespace bqmoe {
 
@@ -118,96 +119,6 @@ __global__ __launch_bounds__(256) void k_dec_logits(const uint16_t* __restrict__
     }
     if (j == 0) *reinterpret_cast<uint4*>(xsum + ((size_t)t * G + g) * 8) = stage_sums(sw, sm);
   }
-}
-
-// Order-preserving integer key of a logit: a > b as floats iff key(a) >
-// key(b), -0 and +0 share a key (they compare equal), and NaN gets the lowest
-// key of all, so that ranking is a strict total order on (key, index) and
-// every selected id is a valid, distinct expert whatever the inputs.
-__device__ __forceinline__ uint32_t order_key(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;  // NaN
-  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;              // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Wave-wide maximum of a 32-bit value (uniform result): DPP steps inside each
-// 16-lane row, then the four row maxima read as scalars.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
-  v = max(v, dpp_u32<0x140>(v));  // row_mirror
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
-}
-
-// Top-k of one token's E logits by one wave (lane l holds experts l + 64i),
-// larger logit first and the lower index first among equal ones: k rounds,
-// each taking the largest remaining order key (a wave maximum) and, among
-// the entries holding it, the one with the lowest expert index (each lane's
-// candidate is its lowest-index entry with its largest key; the lowest index
-// overall is the first lane of the lowest slot i holding the maximum).
-// Lanes 0..k-1 return the ids in order and their softmax weights
-// exp(l_j - l_0) / sum.  PER = entries per lane, a compile-time bound on E/64.
-template <int PER>
-__device__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, int& my_id,
-                          float& my_w) {
-  constexpr int MAXPER = PER;  // PER * 64 >= E
-  const int per = (E + 63) / 64;
-  float v[MAXPER];
-  uint32_t key[MAXPER];
-  uint32_t avail = 0;  // bit i: entry i present and not yet chosen
-#pragma unroll
-  for (int i = 0; i < MAXPER; ++i) {
-    const int e = lane + 64 * i;
-    const bool present = i < per && e < E;
-    v[i] = present ? L[e] : 0.f;
-    key[i] = order_key(v[i]);
-    if (present) avail |= 1u << i;
-  }
-  float top = 0.f, my_v = 0.f;
-  my_id = -1;
-  for (int j = 0; j < k; ++j) {
-    uint32_t bk = 0u;
-    int bi = -1;
-    float bv = 0.f;
-#pragma unroll
-    for (int i = 0; i < MAXPER; ++i) {
-      const bool better = ((avail >> i) & 1u) && (bi < 0 || key[i] > bk);
-      bk = better ? key[i] : bk;
-      bi = better ? i : bi;
-      bv = better ? v[i] : bv;
-    }
-    const uint32_t kmax = wave_max_u32(bi >= 0 ? bk : 0u);
-    int sel_lane = 0, sel_i = 0;
-#pragma unroll
-    for (int i = 0; i < MAXPER; ++i) {
-      if (i < per) {
-        const uint64_t m = __ballot(bi == i && bk == kmax);
-        if (m) {
-          sel_lane = __ffsll((unsigned long long)m) - 1;
-          sel_i = i;
-          break;
-        }
-      }
-    }
-    const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), sel_lane));
-    if (lane == sel_lane) avail &= ~(1u << sel_i);
-    if (j == 0) top = val;
-    if (lane == j) {
-      my_id = sel_lane + 64 * sel_i;
-      my_v = val;
-    }
-  }
-  const float ex = (lane < k) ? expf(my_v - top) : 0.f;
-  const float den = wave_sum(ex);
-  my_w = ex / den;
 }
 
 // Generic top-k: wave per token.

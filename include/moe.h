@@ -170,7 +170,11 @@ moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T,
  * after the earlier stages have run on that workspace with the same inputs.
  * This is the hook used to time one kernel with events or a profiler, and
  * running the stages in order one call at a time is equivalent to the full
- * call.  An empty or unknown mask returns MOE_ERR_INVALID_ARG. */
+ * call.  For a single token and at most 256 experts, the decode gate/up stage
+ * makes the expert selection itself, from R->logits, and writes everything
+ * the select stage writes (same values). A call whose mask holds both SELECT
+ * and GATEUP then launches no separate select kernel.  An empty or unknown
+ * mask returns MOE_ERR_INVALID_ARG. */
 enum {
   MOE_DECODE_STAGE_ROUTE = 1u,   /* router logits + activation staging */
   MOE_DECODE_STAGE_SELECT = 2u,  /* top-k, weights, permutation, active-expert list */
