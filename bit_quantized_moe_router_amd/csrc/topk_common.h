@@ -22,8 +22,7 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide maximum of a 32-bit value (uniform result): DPP steps inside each
-// 16-lane row, then the four row maxima read as scalars.
+// One DPP lane move of a 32-bit value inside 16-lane rows.
 // (bound_ctrl: a lane without a source would read 0, the identity of an
 // unsigned maximum; these patterns have none, and the form lets the compiler
 // fold the lane move into the max instruction.)
@@ -31,95 +30,82 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+
+// Wave-wide maximum of a 32-bit value, left in every lane without scalar
+// steps: the DPP steps leave each 16-lane row's maximum in all of its lanes,
+// then the gfx950 lane swaps pair row 2m with row 2m+1 and the lower with the
+// upper half.
+__device__ __forceinline__ uint32_t wave_allmax_u32(uint32_t v) {
   v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
   v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
   v = max(v, dpp_u32<0x141>(v));  // row_half_mirror
   v = max(v, dpp_u32<0x140>(v));  // row_mirror
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)p[0], (uint32_t)p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)q[0], (uint32_t)q[1]);
+}
+
+// The logit back from its order key (key 1, NaN's, gives a NaN; -0 comes
+// back as +0, which weighs the same).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
 // Top-k of one token's E logits by one wave (lane l holds experts l + 64i),
 // larger logit first and the lower index first among equal ones.  Each lane
-// first sorts its PER entries by (key descending, index ascending); then k
-// rounds each take the largest head key of the wave (a wave maximum), the
-// lowest expert index among the lanes whose head holds it (one ballot, and
-// only on a tie across lanes one more per entry slot), and pop that lane's
-// head.  Lanes 0..k-1 return the ids in order and their softmax weights
+// first sorts its PER entries by (key descending, index ascending); then each
+// of k rounds takes the largest head key of the wave, the lowest expert index
+// among the heads holding it (a second maximum, of inverted indices) and pops
+// that lane's head.  Every step runs in all lanes with vector operations only
+// (wave_allmax_u32), so a round is a short chain with no scalar round trips.
+// Lanes 0..k-1 return the ids in order and their softmax weights
 // exp(l_j - l_0) / sum.  PER = entries per lane, a compile-time bound on E/64.
 template <int PER>
 __device__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, int& my_id,
                           float& my_w) {
   const int per = (E + 63) / 64;
   uint32_t key[PER];
-  float v[PER];
   int ix[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
     const bool present = i < per && e < E;
-    v[i] = present ? L[present ? e : 0] : 0.f;
-    key[i] = present ? order_key(v[i]) : 0u;
-    ix[i] = i;
+    key[i] = present ? order_key(L[present ? e : 0]) : 0u;
+    ix[i] = e;
   }
-  // odd-even transposition sort of the lane's entries
+  // odd-even transposition sort of the lane's entries (indices ascend with i)
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
 #pragma unroll
     for (int i = p & 1; i + 1 < PER; i += 2) {
       const bool sw = key[i + 1] > key[i] || (key[i + 1] == key[i] && ix[i + 1] < ix[i]);
       const uint32_t ka = key[i], kb = key[i + 1];
-      const float va = v[i], vb = v[i + 1];
       const int ia = ix[i], ib = ix[i + 1];
       key[i] = sw ? kb : ka;
       key[i + 1] = sw ? ka : kb;
-      v[i] = sw ? vb : va;
-      v[i + 1] = sw ? va : vb;
       ix[i] = sw ? ib : ia;
       ix[i + 1] = sw ? ia : ib;
     }
   }
-  float top = 0.f, my_v = 0.f;
+  uint32_t top = 0u, my_key = 0u;
   my_id = -1;
   for (int j = 0; j < k; ++j) {
-    const uint32_t kmax = wave_max_u32(key[0]);
-    const uint64_t m = __ballot(key[0] == kmax);
-    int sel_lane, sel_i;
-    if (__popcll(m) == 1) {
-      sel_lane = __ffsll((unsigned long long)m) - 1;
-      sel_i = __builtin_amdgcn_readlane(ix[0], sel_lane);
-    } else {  // equal keys in several lanes: lowest entry slot, then lowest lane
-      sel_lane = 0;
-      sel_i = 0;
+    const uint32_t kmax = wave_allmax_u32(key[0]);
+    // lowest expert index among the heads equal to kmax: max of ~index
+    const uint32_t win = ~wave_allmax_u32(key[0] == kmax ? ~(uint32_t)ix[0] : 0u);
+    const bool pop = (uint32_t)ix[0] == win;  // the winning lane pops its head
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const uint64_t mi = __ballot(key[0] == kmax && ix[0] == i);
-        if (mi) {
-          sel_lane = __ffsll((unsigned long long)mi) - 1;
-          sel_i = i;
-          break;
-        }
-      }
+    for (int t = 0; t + 1 < PER; ++t) {
+      key[t] = pop ? key[t + 1] : key[t];
+      ix[t] = pop ? ix[t + 1] : ix[t];
     }
-    const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[0]), sel_lane));
-    if (lane == sel_lane) {  // pop the head
-#pragma unroll
-      for (int t = 0; t + 1 < PER; ++t) {
-        key[t] = key[t + 1];
-        v[t] = v[t + 1];
-        ix[t] = ix[t + 1];
-      }
-      key[PER - 1] = 0u;
-    }
-    if (j == 0) top = val;
-    if (lane == j) {
-      my_id = sel_lane + 64 * sel_i;
-      my_v = val;
-    }
+    key[PER - 1] = pop ? 0u : key[PER - 1];
+    top = j == 0 ? kmax : top;
+    my_key = lane == j ? kmax : my_key;
+    my_id = lane == j ? (int)win : my_id;
   }
-  const float ex = (lane < k) ? expf(my_v - top) : 0.f;
+  const float ex = (lane < k) ? expf(key_value(my_key) - key_value(top)) : 0.f;
   const float den = wave_sum(ex);
   my_w = ex / den;
 }
