@@ -32,7 +32,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["bit_quantized_moe_router_amd/csrc/decode.hip",
-                  "bit_quantized_moe_router_amd/csrc/device_common.h"]
+                  "bit_quantized_moe_router_amd/csrc/device_common.h",
+                  "bit_quantized_moe_router_amd/csrc/topk_common.h"]
 
 
 def log(*a):
@@ -168,17 +169,20 @@ def decode_leg(args, dev):
             bq.moe_forward_decode_stages(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j], st)
         torch.cuda.synchronize()
         return None
+    # back-to-back launches between one pair of events on the launch stream:
+    # the average includes the short gap between consecutive kernels
     reps = max(K, 8 * C)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
+    for r in range(C):
+        bq.moe_forward_decode_stages(handles[r], xd[r], T, 0, Rs[r], wss[r], outs[r], GU)
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a_ev.record()
     for r in range(reps):
         j = r % C
-        evs[r][0].record()
         bq.moe_forward_decode_stages(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j], GU)
-        evs[r][1].record()
+    b_ev.record()
     torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3  # us
-    gu_us = float(np.mean(durs))
+    gu_us = a_ev.elapsed_time(b_ev) * 1e3 / reps
     gu_b = float(np.mean([gu_bytes[r % C] for r in range(reps)]))
     traffic = measured_traffic("k_dec_gateup")
     roof = {"kernel": "k_dec_gateup (decode gate/up + SiLU)", "bound": "hbm",

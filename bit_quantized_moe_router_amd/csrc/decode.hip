@@ -61,7 +61,12 @@ __device__ __forceinline__ int dec_src_row(int c, bool gather, int base, uint32_
 //    the down projection the fetched (W, S) half sums are turned into staged
 //    sums on the way.
 __host__ __device__ constexpr int ring_row_stride() { return 256 + 16; }
-__host__ __device__ constexpr int ring_bytes(int rc) { return rc * (ring_row_stride() + 64); }
+// staged sums of a row: 64 B, at a stride of 80 B (8 rows' 16-B reads then hit
+// disjoint LDS banks; at 64 B rows r and r + 4 would share them)
+__host__ __device__ constexpr int ring_sum_stride() { return 64 + 16; }
+__host__ __device__ constexpr int ring_bytes(int rc) {
+  return rc * (ring_row_stride() + ring_sum_stride());
+}
 // LDS of one wave, rounded to 256 B
 __host__ __device__ constexpr int ring_wave_bytes(int rc) { return (ring_bytes(rc) + 255) & ~255; }
 
@@ -110,7 +115,9 @@ __device__ __forceinline__ void dec_kb_store(uint8_t* buf, const KbRegs<RC>& v, 
                                 __uint_as_float(sv[1]) + __uint_as_float(sv[3]));
     sv = u32x4{st.x, st.y, st.z, st.w};
   }
-  *reinterpret_cast<u32x4*>(buf + RC * ring_row_stride() + (lane & (RC * 4 - 1)) * 16) = sv;
+  const int slot = lane & (RC * 4 - 1);  // row slot / 4, group slot % 4
+  *reinterpret_cast<u32x4*>(buf + RC * ring_row_stride() + (slot >> 2) * ring_sum_stride() +
+                            (slot & 3) * 16) = sv;
 }
 
 // 2. Packed tiles of one of a wave's k-blocks (kb0 + i) for NS streams: codes
@@ -152,9 +159,9 @@ __device__ __forceinline__ void dec_load_kb(int i, u32x2 (&wc)[KBW][NS], uint32_
 // 3. Matrix-core work on one k-block; per 32-group one correction op (two if
 //    the projections differ) and one op per stream; the group's scale
 //    multiplies MR accumulator rows (rows 4*(lane/16) + i carry real rows for
-//    i < M; MR = 1 when M == 1).  A and the sums come from the k-block's LDS
-//    buffer.  GUARD: a k-block past the wave's range (live false) adds zero,
-//    through a zero scale.
+//    i < M; MR = M for M <= 2, else 4).  A and the sums come from the
+//    k-block's LDS buffer.  GUARD: a k-block past the wave's range (live
+//    false) adds zero, through a zero scale.
 template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int MR, bool GUARD>
 __device__ __forceinline__ void dec_mfma_kb(int i, f32x4 (&acc)[NS], const u32x2 (&wc)[KBW][NS],
                                             const uint32_t (&wh)[KBW][NS],
@@ -231,7 +238,7 @@ __device__ __forceinline__ void dec_pipeline(
     dec_kb_store<RC, !GATEUP>(buf, v[i], lane);
     dec_mfma_kb<NS, GATEUP, QA3, QB3, SAMEC, KBW, MR, !FULL>(
         i, acc, wc, wh, ws, buf + arow * ring_row_stride() + q * 16,
-        buf + RC * ring_row_stride() + arow * 64, bca, bcb, ur, i < nkb);
+        buf + RC * ring_row_stride() + arow * ring_sum_stride(), bca, bcb, ur, i < nkb);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -490,6 +497,10 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
       dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 1, 1, true>(
           acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
           row0, tok3, A, Asum, K, bca, bcb, ur);
+    else if (M == 2)
+      dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 2, 2, true>(
+          acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
+          row0, tok3, A, Asum, K, bca, bcb, ur);
     else
       dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 4, kDecMaxRows, true>(
           acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
@@ -611,6 +622,10 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
             row0, 0u, hs, hsum, K, bc, bc, ur);
       else if (M == 1)
         dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 1, 1, true>(
+            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
+            row0, 0u, hs, hsum, K, bc, bc, ur);
+      else if (M == 2)
+        dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 2, 2, true>(
             acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
             row0, 0u, hs, hsum, K, bc, bc, ur);
       else
