@@ -28,7 +28,11 @@ namespace bqmoe {
 
 constexpr int kRows = kPrefillTileM;  // rows per tile (two 32-row matrix-core tiles)
 
-__device__ __forceinline__ float silu_pf(float g) { return g / (1.0f + expf(-g)); }
+// SiLU with the hardware exp2 and reciprocal (a few fp32 ulp; h is rounded
+// to bf16 right after, whose unit is 2^16 times coarser)
+__device__ __forceinline__ float silu_pf(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
 
 // Activation staging for prefill: xs = x/16 and the 32-group sums (W, S).
 __global__ __launch_bounds__(256) void k_stage(const uint16_t* __restrict__ x, int T, int d,
@@ -268,6 +272,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
     // of the down projection
     const int I = N;
     const float wgt = slot_weight(l32);
+    // the (W, S) sums of row slot c = 16 rt + i end up in lane c of each
+    // half, which stages them: one stage_sums per lane instead of per row
+    float my_w = 0.f, my_s = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
@@ -283,11 +290,14 @@ __global__ __launch_bounds__(256, 2) void k_pf_gemm(
           hs_part += __shfl_xor(hs_part, o, 32);
           hw_part += __shfl_xor(hw_part, o, 32);
         }
-        if (m < M && l32 == 0)
-          *reinterpret_cast<uint4*>(out_sum + ((size_t)(row0 + m) * (I / 32) + cw) * 8) =
-              stage_sums(hw_part, hs_part);
+        my_w = l32 == rt * 16 + i ? hw_part : my_w;
+        my_s = l32 == rt * 16 + i ? hs_part : my_s;
       }
     }
+    const int mrow = (l32 >> 4) * 32 + 8 * ((l32 & 15) >> 2) + 4 * hl + (l32 & 3);
+    if (mrow < M)
+      *reinterpret_cast<uint4*>(out_sum + ((size_t)(row0 + mrow) * (I / 32) + cw) * 8) =
+          stage_sums(my_w, my_s);
   } else {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
