@@ -29,7 +29,8 @@ MOE_PREFILL_STAGE_ROUTE, MOE_PREFILL_STAGE_STAGE_X, MOE_PREFILL_STAGE_GATEUP, \
     MOE_PREFILL_STAGE_DOWN, MOE_PREFILL_STAGE_COMBINE = 1, 2, 4, 8, 16
 MOE_PREFILL_STAGES_ALL = 31
 
-EXPORTED = ("moe_packed_bytes", "moe_expert_bytes", "moe_pack_weights", "moe_workspace_bytes",
+EXPORTED = ("moe_packed_bytes", "moe_expert_bytes", "moe_pack_weights", "moe_quantize_rtn",
+            "moe_workspace_bytes",
             "moe_route_topk", "moe_forward_decode", "moe_forward_prefill",
             "moe_forward_decode_stages", "moe_forward_prefill_stages", "moe_status_string",
             "moe_abi_version")
@@ -80,6 +81,7 @@ def load():
     lib.moe_expert_bytes.argtypes, lib.moe_expert_bytes.restype = [i32, i32, i32, i64, i64], sz
     lib.moe_pack_weights.argtypes, lib.moe_pack_weights.restype = [i32, i64, i64, vp, vp, vp,
                                                                    sz], i32
+    lib.moe_quantize_rtn.argtypes, lib.moe_quantize_rtn.restype = [i32, i64, i64, vp, vp, vp], i32
     lib.moe_workspace_bytes.argtypes, lib.moe_workspace_bytes.restype = [L, ctypes.c_int32], sz
     lib.moe_route_topk.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp]
     lib.moe_forward_decode.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, vp]
@@ -146,6 +148,18 @@ def moe_pack_weights(qtype: int, codes: np.ndarray, scales: np.ndarray,
     st = load().moe_pack_weights(qtype, K, N, _ptr(codes), _ptr(scales), _ptr(out), out.nbytes)
     _check(st, "moe_pack_weights")
     return out[:nbytes]
+
+
+def moe_quantize_rtn(qtype: int, w: np.ndarray):
+    """Round-to-nearest codes [N][K] (uint8) and fp16 scale bits [N][K/32] of float weights
+    w[N][K] on the host (moe_quantize_rtn)."""
+    w = np.ascontiguousarray(w, np.float32)
+    N, K = w.shape
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, max(K // 32, 1)), np.uint16)
+    st = load().moe_quantize_rtn(qtype, K, N, _ptr(w), _ptr(codes), _ptr(scales))
+    _check(st, "moe_quantize_rtn")
+    return codes, scales[:, : K // 32]
 
 
 # -------------------------------------------------------------- layer

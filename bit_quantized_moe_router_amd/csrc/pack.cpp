@@ -8,6 +8,7 @@
 // single mask-and-or turns a pair of fields into a pair of bf16 operands.
 // Bit 2 of a 3-bit level (plane 1) is placed so that one shift lines up pairs
 // 0..2 of a group just above their low bits and another shift pair 3.
+#include <cmath>
 #include <cstring>
 
 #include "moe_internal.h"
@@ -53,6 +54,57 @@ extern "C" size_t moe_expert_bytes(int qg, int qu, int qd, int64_t d, int64_t in
          dn = moe_packed_bytes(qd, inter, d);
   if (!g || !u || !dn) return 0;
   return g + u + dn;  // each is a multiple of 256
+}
+
+// Nearest fp16 value of a finite, non-negative double, ties to even (fp16:
+// 11 significant bits, smallest subnormal 2^-24, largest finite 65504);
+// returns 0x7C00 (infinity) past the largest finite value.
+static uint16_t round_to_f16(double v) {
+  if (v == 0.0) return 0;
+  int e;
+  std::frexp(v, &e);             // v = m * 2^e, m in [0.5, 1)
+  int q = e - 11;                // unit in the last place of an 11-bit significand
+  if (q < -24) q = -24;          // subnormal spacing
+  const double units = std::nearbyint(std::ldexp(v, -q));  // ties to even (default mode)
+  const double r = std::ldexp(units, q);
+  if (r > 65504.0) return 0x7C00;
+  if (r < 0x1p-14) return (uint16_t)units;  // subnormal: the significand is the code
+  int re;
+  const double rm = std::frexp(r, &re);      // r = rm * 2^re, rm in [0.5, 1)
+  const uint32_t mant = (uint32_t)std::ldexp(rm, 11) - 1024u;  // 10 fraction bits
+  return (uint16_t)(((re - 1 + 15) << 10) | mant);
+}
+
+static double f16_value(uint16_t h) {
+  const int ex = (h >> 10) & 31, man = h & 1023;
+  return ex == 0 ? std::ldexp((double)man, -24) : std::ldexp((double)(man | 1024), ex - 25);
+}
+
+extern "C" moe_status moe_quantize_rtn(int qtype, int64_t K, int64_t N, const float* w,
+                                       uint8_t* codes, uint16_t* scales) {
+  const int levels = qtype_levels(qtype);
+  if (levels == 0 || K <= 0 || N <= 0 || K % 32) return MOE_ERR_UNSUPPORTED;
+  if (!w || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  const double off = qtype_offset(qtype), cmax = (levels - 1) - off;
+  for (int64_t i = 0; i < K * N; ++i)
+    if (!std::isfinite(w[i])) return MOE_ERR_INVALID_ARG;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t g = 0; g < K / 32; ++g) {
+      const float* wg = w + n * K + g * 32;
+      double amax = 0.0;
+      for (int j = 0; j < 32; ++j) amax = std::fmax(amax, std::fabs((double)wg[j]));
+      const uint16_t sh = round_to_f16(amax / cmax);
+      if (sh == 0x7C00) return MOE_ERR_INVALID_ARG;
+      scales[n * (K / 32) + g] = sh;
+      const double s = f16_value(sh);
+      for (int j = 0; j < 32; ++j) {
+        double u = s > 0.0 ? std::nearbyint((double)wg[j] / s + off) : std::nearbyint(off);
+        u = std::fmin(std::fmax(u, 0.0), (double)(levels - 1));
+        codes[n * K + g * 32 + j] = (uint8_t)u;
+      }
+    }
+  }
+  return MOE_OK;
 }
 
 extern "C" moe_status moe_pack_weights(int qtype, int64_t K, int64_t N, const uint8_t* codes,

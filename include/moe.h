@@ -107,6 +107,25 @@ size_t moe_expert_bytes(int q_gate, int q_up, int q_down, int64_t d, int64_t int
 moe_status moe_pack_weights(int qtype, int64_t K, int64_t N, const uint8_t* codes,
                             const uint16_t* scales, void* out, size_t out_bytes);
 
+/* Round-to-nearest quantisation of float weights into the code alphabet of
+ * qtype, the input moe_pack_weights takes.  Per column n and 32-group g
+ * along K, the scale is s = fp16(max |w| / cmax), rounded to nearest even,
+ * where cmax = (levels - 1) - offset is the largest level magnitude (ternary
+ * 1, int2 1.5, int3 3.5); each code is u = round-half-even(w / s + offset),
+ * clamped to 0..levels-1 (u = round-half-even(offset) when s == 0).
+ * Arithmetic in double.  The "Xolotl" README's "Quick start" names the code
+ * families but no quantiser; this is the plain round-to-nearest route from
+ * float weights onto them (the pages' calibrated quantiser is not
+ * reproduced).
+ *   w      : host, [N][K] fp32 (row n holds k = 0..K-1), finite
+ *   codes  : host, [N][K] level indices (output)
+ *   scales : host, [N][K/32] fp16 bit patterns (output)
+ * Returns MOE_ERR_UNSUPPORTED for an unknown qtype or K % 32 != 0,
+ * MOE_ERR_INVALID_ARG for null pointers, a non-finite weight, or a group
+ * whose scale would exceed the largest fp16 value. */
+moe_status moe_quantize_rtn(int qtype, int64_t K, int64_t N, const float* w, uint8_t* codes,
+                            uint16_t* scales);
+
 /* ------------------------------------------------------------------ layer */
 typedef struct {
   int32_t d;          /* hidden size, multiple of 128 */

@@ -54,6 +54,7 @@ def _load():
     lib.oracle_packed_bytes.restype = sz
     lib.oracle_unpack.argtypes = [i32, i64, i64, p, sz, p, p]
     lib.oracle_dequant.argtypes = [i32, i64, i64, p, p, p]
+    lib.oracle_quantize_rtn.argtypes = [i32, i64, i64, p, p, p]
     lib.oracle_router_logits.argtypes = [i32, i32, i32, p, p, p, p]
     lib.oracle_topk_softmax.argtypes = [i32, i32, i32, p, p, p]
     lib.oracle_permute.argtypes = [i32, i32, i32, p, p, p, p, p]
@@ -61,7 +62,8 @@ def _load():
                                        p, p, p]
     lib.oracle_combine.argtypes = [i32, i32, i32, p, p, p, p, p, i32, p, p]
     lib.oracle_moe_layer.argtypes = [i32] * 9 + [p, p, p, i32, p, p, p, i32, p, p, p, p, p, p, p]
-    for name in ("oracle_unpack", "oracle_dequant", "oracle_router_logits", "oracle_topk_softmax",
+    for name in ("oracle_unpack", "oracle_dequant", "oracle_quantize_rtn", "oracle_router_logits",
+                 "oracle_topk_softmax",
                  "oracle_permute", "oracle_expert_rows", "oracle_combine", "oracle_moe_layer"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -123,6 +125,16 @@ def unpack(qtype, K, N, blob):
     codes = np.empty((N, K), np.uint8)
     scales = np.empty((N, K // 32), np.uint16)
     _ok(_load().oracle_unpack(qtype, K, N, _p(blob), blob.nbytes, _p(codes), _p(scales)), "unpack")
+    return codes, scales
+
+
+def quantize_rtn(qtype, w):
+    """Round-to-nearest codes [N][K] and fp16 scale bits [N][K/32] of float weights w[N][K]."""
+    w = _c(w, np.float32)
+    N, K = w.shape
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, K // 32), np.uint16)
+    _ok(_load().oracle_quantize_rtn(qtype, K, N, _p(w), _p(codes), _p(scales)), "quantize_rtn")
     return codes, scales
 
 

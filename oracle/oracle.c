@@ -180,6 +180,61 @@ int oracle_unpack(int qtype, int64_t K, int64_t N, const uint8_t* blob, size_t b
   return 0;
 }
 
+/* ------------------------------------------------------- quantise (RTN) */
+
+/* fp16 nearest to a finite v >= 0, ties to even, as bits; 0x7C00 past 65504.
+ * Written from the fp16 definition: in the binade [2^e, 2^(e+1)) (e >= -14)
+ * the representable values are multiples of 2^(e-10); below 2^-14 they are
+ * multiples of 2^-24.  Take the two neighbours and keep the nearer. */
+static uint16_t oracle_f64_to_f16(double v) {
+  if (v == 0.0) return 0;
+  int e = ilogb(v);
+  if (e < -14) e = -14;
+  double ulp = ldexp(1.0, e - 10);
+  double lo = floor(v / ulp) * ulp, hi = lo + ulp, r;
+  if (v - lo < hi - v) r = lo;
+  else if (hi - v < v - lo) r = hi;
+  else r = fmod(lo / ulp, 2.0) == 0.0 ? lo : hi;   /* tie: even multiple */
+  if (r > 65504.0) return 0x7C00;
+  if (r < ldexp(1.0, -14)) return (uint16_t)(r / ldexp(1.0, -24));
+  int E = ilogb(r);                                 /* r = 1.f * 2^E */
+  double frac = r / ldexp(1.0, E) - 1.0;            /* in [0, 1), multiple of 2^-10 */
+  return (uint16_t)(((E + 15) << 10) | (int)(frac * 1024.0));
+}
+
+/* Round-to-nearest quantisation, the reading in moe.h: per column n and
+ * 32-group g, s = fp16(max|w| / cmax) with cmax = (levels-1) - offset, and
+ * u = clamp(round-half-even(w / s + offset), 0, levels-1); u = round(offset)
+ * when s == 0.  Returns -1 for a bad qtype or shape or a non-finite weight
+ * or a scale past the fp16 range. */
+int oracle_quantize_rtn(int qtype, int64_t K, int64_t N, const float* w, uint8_t* codes,
+                        uint16_t* scales) {
+  int levels = oracle_code_levels(qtype);
+  if (levels == 0 || K <= 0 || N <= 0 || K % 32) return -1;
+  double off = oracle_code_offset(qtype), cmax = (levels - 1) - off;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t g = 0; g < K / 32; ++g) {
+      double amax = 0.0;
+      for (int64_t k = g * 32; k < g * 32 + 32; ++k) {
+        double a = fabs((double)w[n * K + k]);
+        if (!isfinite(a)) return -1;
+        if (a > amax) amax = a;
+      }
+      uint16_t sb = oracle_f64_to_f16(amax / cmax);
+      if (sb == 0x7C00) return -1;
+      scales[n * (K / 32) + g] = sb;
+      double s = oracle_f16_to_f64(sb);
+      for (int64_t k = g * 32; k < g * 32 + 32; ++k) {
+        double u = s > 0.0 ? nearbyint((double)w[n * K + k] / s + off) : nearbyint(off);
+        if (u < 0.0) u = 0.0;
+        if (u > levels - 1) u = levels - 1;
+        codes[n * K + k] = (uint8_t)u;
+      }
+    }
+  }
+  return 0;
+}
+
 /* -------------------------------------------------------------- dequantise */
 
 int oracle_dequant(int qtype, int64_t K, int64_t N, const uint8_t* codes, const uint16_t* scales,

@@ -31,6 +31,11 @@ double oracle_f16_to_f64(uint16_t h);
 double oracle_code_offset(int qtype);
 int oracle_code_levels(int qtype);
 
+/* Round-to-nearest quantisation of float weights w[N][K] into codes[N][K] and
+ * fp16 scales[N][K/32] (the reading stated in moe.h); 0, or -1 on bad input. */
+int oracle_quantize_rtn(int qtype, int64_t K, int64_t N, const float* w, uint8_t* codes,
+                        uint16_t* scales);
+
 /* Packed format v2: decode a blob back to canonical codes [N][K] and scales [N][K/32]. */
 size_t oracle_packed_bytes(int qtype, int64_t K, int64_t N);
 int oracle_unpack(int qtype, int64_t K, int64_t N, const uint8_t* blob, size_t blob_bytes,
