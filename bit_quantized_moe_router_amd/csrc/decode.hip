@@ -67,8 +67,11 @@ __host__ __device__ constexpr int ring_sum_stride() { return 64 + 16; }
 __host__ __device__ constexpr int ring_bytes(int rc) {
   return rc * (ring_row_stride() + ring_sum_stride());
 }
-// LDS of one wave, rounded to 256 B
-__host__ __device__ constexpr int ring_wave_bytes(int rc) { return (ring_bytes(rc) + 255) & ~255; }
+// LDS of one wave, rounded to 256 B, then 256 B of zeros (the A operand of
+// band rows that hold no row; see the band pipeline)
+__host__ __device__ constexpr int ring_wave_bytes(int rc) {
+  return ((ring_bytes(rc) + 255) & ~255) + 256;
+}
 
 template <int RC>
 struct KbRegs {
@@ -133,9 +136,11 @@ __host__ __device__ constexpr int dec_kb_loads() {
   return (2 + (QA3 ? 1 : 0)) + (NS - 1) * (2 + ((GATEUP ? QB3 : QA3) ? 1 : 0));
 }
 
-template <int NS, bool GATEUP, bool QA3, bool QB3, int KBW, bool CLAMP>
+//    With WS = uint32_t (single-row k-blocks, below) a lane loads just the
+//    scale of group lane / 16 of its column (2 B).
+template <int NS, bool GATEUP, bool QA3, bool QB3, int KBW, bool CLAMP, typename WS>
 __device__ __forceinline__ void dec_load_kb(int i, u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS],
-                                            u32x2 (&ws)[KBW][NS],
+                                            WS (&ws)[KBW][NS],
                                             const uint8_t* const (&code_base)[2],
                                             const size_t (&plane1)[2],
                                             const size_t (&scale_off)[2], const int (&nt)[NS],
@@ -152,7 +157,11 @@ __device__ __forceinline__ void dec_load_kb(int i, u32x2 (&wc)[KBW][NS], uint32_
     wh[i][j] =
         q3 ? *reinterpret_cast<const uint32_t*>(base + plane1[second] + tile * 256 + lane * 4)
            : 0u;
-    ws[i][j] = *reinterpret_cast<const u32x2*>(base + scale_off[second] + tile * 128 + r * 8);
+    if constexpr (std::is_same_v<WS, uint32_t>)
+      ws[i][j] = *reinterpret_cast<const uint16_t*>(base + scale_off[second] + tile * 128 + r * 8 +
+                                                    (lane >> 4) * 2);
+    else
+      ws[i][j] = *reinterpret_cast<const u32x2*>(base + scale_off[second] + tile * 128 + r * 8);
   }
 }
 
@@ -243,15 +252,144 @@ __device__ __forceinline__ void dec_pipeline(
   }
 }
 
-// 4'. The same for a single-token launch: the wave's whole slice of the row
-//     (KBW k-blocks, [KBW][256 B], then the sums [KBW][64 B]) is fetched into
-//     registers ahead of the first tiles and written to LDS once; a k-block's
-//     work then only reads LDS.  Lanes read the same row: LDS broadcasts.
-__host__ __device__ constexpr int one_wave_bytes(int kbw) { return kbw * (256 + 64); }
+// 3'. Matrix-core work on a k-block of at most 4 rows (MR).  The k-block's
+//     four 32-groups go to accumulator row bands 4g .. 4g + MR - 1: for group
+//     g the A operand is the rows' group g in band g and zeros elsewhere
+//     (lanes of the other rows read a zeroed LDS area), so the four ops of a
+//     stream add to disjoint rows of one accumulator.  One correction op, its
+//     A operand the four groups' staged sums in the same rows, starts that
+//     accumulator.  Lane l then holds group l / 16 of column l % 16 for rows
+//     0 .. MR-1 in elements 0 .. MR-1 and applies that group's scale with MR
+//     FMAs (one 2-byte scale load per lane).  The four lane quarters are
+//     added at the end of the wave's range.
+template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int MR, int ASTRIDE,
+          int SSTRIDE, bool GUARD>
+__device__ __forceinline__ void dec_mfma_kb_band(int i, f32x4 (&acc)[NS],
+                                                 const u32x2 (&wc)[KBW][NS],
+                                                 const uint32_t (&wh)[KBW][NS],
+                                                 const uint32_t (&ws)[KBW][NS],
+                                                 const uint8_t* a0, const uint8_t* a1,
+                                                 const uint8_t* a2, const uint8_t* a3,
+                                                 const uint8_t* sp, u32x4 bca, u32x4 bcb,
+                                                 const Unpack2R& ur, bool live) {
+  const u32x4 sv = *reinterpret_cast<const u32x4*>(sp + i * SSTRIDE);
+  const f32x4 corr_a = mfma_corr(sv, bca);
+  f32x4 corr_b = corr_a;
+  if constexpr (!SAMEC) corr_b = mfma_corr(sv, bcb);
+  f32x4 d[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) d[j] = (GATEUP && j == 1) ? corr_b : corr_a;
+#pragma unroll
+  for (int GB = 0; GB < 4; ++GB) {
+    const uint8_t* ap = GB == 0 ? a0 : GB == 1 ? a1 : GB == 2 ? a2 : a3;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(ap + i * ASTRIDE);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const bool second = GATEUP && j == 1;
+      const bool q3 = second ? QB3 : QA3;
+      const uint32_t word = (GB < 2) ? wc[i][j][0] : wc[i][j][1];
+      u32x4 b;
+      if (q3) {
+        if (GB == 0) b = unpack3<0>(word, wh[i][j], ur);
+        if (GB == 1) b = unpack3<1>(word, wh[i][j], ur);
+        if (GB == 2) b = unpack3<2>(word, wh[i][j], ur);
+        if (GB == 3) b = unpack3<3>(word, wh[i][j], ur);
+      } else {
+        b = (GB & 1) ? unpack2_r<1>(word, ur) : unpack2_r<0>(word, ur);
+      }
+      d[j] = mfma32(a, b, d[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    float s = f16_to_f32(ws[i][j]);
+    if constexpr (GUARD) s = live ? s : 0.f;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[j][m] = fmaf(s, d[j][m], acc[j][m]);
+  }
+}
+
+// The four lane quarters (groups) of a column added: lanes 0..15 then hold
+// rows 0..MR-1 in elements 0..MR-1, the matrix-core layout of rows 0..3.
+template <int NS, int MR>
+__device__ __forceinline__ void dec_band_fold(f32x4 (&acc)[NS]) {
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float v = m < MR ? acc[j][m] : 0.f;
+      if (m < MR) {
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+      }
+      acc[j][m] = v;
+    }
+}
+
+// 4b. dec_pipeline for slots of at most 4 rows (MR: 1, 2 or 4; RC >= M) in
+//     the banded form of step 3': the rows' groups go to row bands of the
+//     accumulator, so a k-block takes one correction op and MR FMAs per
+//     stream.  The wave's LDS buffer is the same as dec_pipeline's, its zeroed
+//     256 B at the end.  On return rows 0..M-1 sit in lanes 0..15, elements
+//     0..M-1.
+template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, int MR, int RC,
+          bool FULL>
+__device__ __forceinline__ void dec_pipeline_bandr(
+    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], uint32_t (&ws)[KBW][NS],
+    const uint8_t* const (&code_base)[2], const size_t (&plane1)[2], const size_t (&scale_off)[2],
+    const int (&nt)[NS], int KB, int kb0, int nkb, int lane, uint8_t* buf, int M, bool gather,
+    int row0, uint32_t tok3, const uint16_t* __restrict__ A, const uint8_t* __restrict__ Asum,
+    int K, u32x4 bca, u32x4 bcb, const Unpack2R& ur) {
+  static_assert(MR <= 4 && RC >= MR, "band rows");
+  uint8_t* zbuf = buf + ring_wave_bytes(RC) - 256;
+  *reinterpret_cast<u32x4*>(zbuf + (lane & 15) * 16) = u32x4{0u, 0u, 0u, 0u};
+  // per-lane operand addresses: lane l reads row c = l % 4 of group g = (l % 16) / 4
+  const int q = lane >> 4, c = lane & 3, g = (lane >> 2) & 3;
+  const bool real = c < M;
+  const uint8_t* a0 = (real && g == 0 ? buf + c * ring_row_stride() : zbuf) + q * 16;
+  const uint8_t* a1 = (real && g == 1 ? buf + c * ring_row_stride() + 64 : zbuf + 64) + q * 16;
+  const uint8_t* a2 = (real && g == 2 ? buf + c * ring_row_stride() + 128 : zbuf + 128) + q * 16;
+  const uint8_t* a3 = (real && g == 3 ? buf + c * ring_row_stride() + 192 : zbuf + 192) + q * 16;
+  const uint8_t* sp = (lane < 16 && real) ? buf + RC * ring_row_stride() + c * ring_sum_stride() +
+                                                g * 16
+                                          : zbuf;
+  KbRegs<RC> v[KBW];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    dec_kb_fetch<RC, !FULL>(v[i], lane, M, gather, row0, tok3, A, Asum, K,
+                            FULL ? kb0 + i : min(kb0 + i, KB - 1));
+    dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i, wc, wh, ws, code_base, plane1, scale_off, nt,
+                                                  KB, kb0, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    if (i + PRE < KBW) {
+      dec_kb_fetch<RC, !FULL>(v[i + PRE], lane, M, gather, row0, tok3, A, Asum, K,
+                              FULL ? kb0 + i + PRE : min(kb0 + i + PRE, KB - 1));
+      dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i + PRE, wc, wh, ws, code_base, plane1,
+                                                    scale_off, nt, KB, kb0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dec_kb_store<RC, !GATEUP>(buf, v[i], lane);
+    dec_mfma_kb_band<NS, GATEUP, QA3, QB3, SAMEC, KBW, MR, 0, 0, !FULL>(
+        i, acc, wc, wh, ws, a0, a1, a2, a3, sp, bca, bcb, ur, i < nkb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  dec_band_fold<NS, MR>(acc);
+}
+
+// 4'. The pipeline of a single-token launch: the wave's whole slice of the
+//     row (KBW k-blocks, [KBW][256 B], then the sums [KBW][64 B]) is fetched
+//     into registers ahead of the first tiles and written to LDS once, next
+//     to a zeroed area of [KBW][256 B]; a k-block's work then only reads LDS.
+//     On return acc[j][0] of lanes 0..15 holds the wave's sum for column
+//     lane (the other elements are zero).
+__host__ __device__ constexpr int one_wave_bytes(int kbw) { return kbw * (256 + 64 + 256); }
 
 template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, bool FULL>
-__device__ __forceinline__ void dec_pipeline_one(
-    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], u32x2 (&ws)[KBW][NS],
+__device__ __forceinline__ void dec_pipeline_band(
+    f32x4 (&acc)[NS], u32x2 (&wc)[KBW][NS], uint32_t (&wh)[KBW][NS], uint32_t (&ws)[KBW][NS],
     const uint8_t* const (&code_base)[2], const size_t (&plane1)[2], const size_t (&scale_off)[2],
     const int (&nt)[NS], int KB, int kb0, int nkb, int lane, uint8_t* buf, bool gather, int row0,
     uint32_t tok3, const uint16_t* __restrict__ A, const uint8_t* __restrict__ Asum, int K,
@@ -273,12 +411,14 @@ __device__ __forceinline__ void dec_pipeline_one(
       ((FULL ? kb0 + (spiece >> 2) : min(kb0 + (spiece >> 2), KB - 1)) * 4 + (spiece & 3)) * 16);
 #pragma unroll
   for (int i = 0; i < PRE; ++i)
-    dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i, wc, wh, ws, code_base, plane1, scale_off, nt, KB,
-                                           kb0, lane);
+    dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i, wc, wh, ws, code_base, plane1, scale_off, nt,
+                                                  KB, kb0, lane);
   __builtin_amdgcn_sched_barrier(0);
+  uint8_t* zbuf = buf + KBW * (256 + 64);
 #pragma unroll
   for (int p = 0; p < NPA; ++p) {
     const int piece = (p * 64 + lane) & (KBW * 16 - 1);
+    *reinterpret_cast<u32x4*>(zbuf + piece * 16) = u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(buf + piece * 16) = va[p];
   }
   if constexpr (!GATEUP) {
@@ -288,19 +428,26 @@ __device__ __forceinline__ void dec_pipeline_one(
     vs = u32x4{st.x, st.y, st.z, st.w};
   }
   *reinterpret_cast<u32x4*>(buf + KBW * 256 + spiece * 16) = vs;
-  const int q = lane >> 4;
+  // per-lane operand addresses: group g of a k-block from the slice in the
+  // lanes of row 4g, from the zeroed area in the others
+  const int q = lane >> 4, r16 = lane & 15;
+  const uint8_t* a0 = (r16 == 0 ? buf : zbuf) + q * 16;
+  const uint8_t* a1 = (r16 == 4 ? buf : zbuf) + 64 + q * 16;
+  const uint8_t* a2 = (r16 == 8 ? buf : zbuf) + 128 + q * 16;
+  const uint8_t* a3 = (r16 == 12 ? buf : zbuf) + 192 + q * 16;
+  const uint8_t* sp = (lane < 16 && (lane & 3) == 0) ? buf + KBW * 256 + (lane >> 2) * 16 : zbuf;
 #pragma unroll
   for (int i = 0; i < KBW; ++i) {
     if (i + PRE < KBW) {
-      dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i + PRE, wc, wh, ws, code_base, plane1, scale_off,
-                                             nt, KB, kb0, lane);
+      dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i + PRE, wc, wh, ws, code_base, plane1,
+                                                    scale_off, nt, KB, kb0, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
-    dec_mfma_kb<NS, GATEUP, QA3, QB3, SAMEC, KBW, 1, !FULL>(
-        i, acc, wc, wh, ws, buf + i * 256 + q * 16, buf + KBW * 256 + i * 64, bca, bcb, ur,
-        i < nkb);
+    dec_mfma_kb_band<NS, GATEUP, QA3, QB3, SAMEC, KBW, 1, 256, 64, !FULL>(
+        i, acc, wc, wh, ws, a0, a1, a2, a3, sp, bca, bcb, ur, i < nkb);
     __builtin_amdgcn_sched_barrier(0);
   }
+  dec_band_fold<NS, 1>(acc);
 }
 
 // k-blocks whose tile loads run ahead of the matrix-core work.  Shallow on
@@ -339,6 +486,9 @@ __device__ __forceinline__ void dec_select_one_token(const DecRoute& ro, int slo
   const int tid = threadIdx.x, lane = tid & 63;
   const int k = ro.k;
   if (tid < 64) {
+    // the block's work waits on this chain; other blocks' waves on the SIMD
+    // are already streaming, so it takes the issue slots first
+    __builtin_amdgcn_s_setprio(3);
     int id;
     float w;
     wave_topk<4>(ro.logits, ro.E, k, lane, id, w);
@@ -382,6 +532,7 @@ __device__ __forceinline__ void dec_select_one_token(const DecRoute& ro, int slo
         ro.offsets[ro.E] = k;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
   e = __builtin_amdgcn_readfirstlane(s_slot[0]);
@@ -476,30 +627,36 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x2 wc[KBW][NS];
   uint32_t wh[KBW][NS];
-  u32x2 ws[KBW][NS];
   if constexpr (ONE_ROW) {
+    uint32_t ws[KBW][NS];
     uint8_t* buf = lds + wave * one_wave_bytes(KBW);
     if (nkb < KBW)
-      dec_pipeline_one<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, false>(
+      dec_pipeline_band<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, false>(
           acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, GATEUP,
           row0, tok3, A, Asum, K, bca, bcb, ur);
     else
-      dec_pipeline_one<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, true>(
+      dec_pipeline_band<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, true>(
           acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, GATEUP,
           row0, tok3, A, Asum, K, bca, bcb, ur);
   } else {
+    u32x2 ws[KBW][NS];
+    uint32_t wsb[KBW][NS];
     uint8_t* buf = lds + wave * ring_wave_bytes(kDecMaxRows);
     if (nkb < KBW)
       dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 4, kDecMaxRows, false>(
           acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
           row0, tok3, A, Asum, K, bca, bcb, ur);
     else if (M == 1)
-      dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 1, 1, true>(
-          acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
+      dec_pipeline_bandr<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 1, 1, true>(
+          acc, wc, wh, wsb, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
           row0, tok3, A, Asum, K, bca, bcb, ur);
     else if (M == 2)
-      dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 2, 2, true>(
-          acc, wc, wh, ws, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
+      dec_pipeline_bandr<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 2, 2, true>(
+          acc, wc, wh, wsb, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
+          row0, tok3, A, Asum, K, bca, bcb, ur);
+    else if (M <= 4)
+      dec_pipeline_bandr<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 4, 4, true>(
+          acc, wc, wh, wsb, code_base, plane1, scale_off, nt, KB, kb0, nkb, lane, buf, M, GATEUP,
           row0, tok3, A, Asum, K, bca, bcb, ur);
     else
       dec_pipeline<NS, GATEUP, QA3, QB3, SAMEC, KBW, PRE, 4, kDecMaxRows, true>(
@@ -602,18 +759,19 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
     u32x2 wc[KBW][1];
     uint32_t wh[KBW][1];
     u32x2 ws[KBW][1];
+    uint32_t wsb[KBW][1];
     const u32x4 bc = corr_b_operand(q == 0, cd);
     const Unpack2R ur = {uk.m0, uk.m1, uk.m2, lane_copy(uk.b0), lane_copy(uk.b1),
                          lane_copy(uk.b2)};
     f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
     if constexpr (ONE_ROW) {
       if (KB < KBW)
-        dec_pipeline_one<1, false, Q3, Q3, true, KBW, PRE, false>(
-            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, false, row0,
+        dec_pipeline_band<1, false, Q3, Q3, true, KBW, PRE, false>(
+            acc, wc, wh, wsb, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, false, row0,
             0u, hs, hsum, K, bc, bc, ur);
       else
-        dec_pipeline_one<1, false, Q3, Q3, true, KBW, PRE, true>(
-            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, false, row0,
+        dec_pipeline_band<1, false, Q3, Q3, true, KBW, PRE, true>(
+            acc, wc, wh, wsb, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, false, row0,
             0u, hs, hsum, K, bc, bc, ur);
     } else {
       if (KB < KBW)
@@ -621,12 +779,16 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
             acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
             row0, 0u, hs, hsum, K, bc, bc, ur);
       else if (M == 1)
-        dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 1, 1, true>(
-            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
+        dec_pipeline_bandr<1, false, Q3, Q3, true, KBW, PRE, 1, 1, true>(
+            acc, wc, wh, wsb, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
             row0, 0u, hs, hsum, K, bc, bc, ur);
       else if (M == 2)
-        dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 2, 2, true>(
-            acc, wc, wh, ws, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
+        dec_pipeline_bandr<1, false, Q3, Q3, true, KBW, PRE, 2, 2, true>(
+            acc, wc, wh, wsb, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
+            row0, 0u, hs, hsum, K, bc, bc, ur);
+      else if (M <= 4)
+        dec_pipeline_bandr<1, false, Q3, Q3, true, KBW, PRE, 4, 4, true>(
+            acc, wc, wh, wsb, code_base, plane1, scale_off, ntl, KB, 0, KB, lane, buf, M, false,
             row0, 0u, hs, hsum, K, bc, bc, ur);
       else
         dec_pipeline<1, false, Q3, Q3, true, KBW, PRE, 4, kDecMaxRows, true>(
