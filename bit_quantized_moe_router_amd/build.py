@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbqmoe.so")
 
-SOURCES = ["pack.cpp", "api.cpp", "route.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["pack.cpp", "api.cpp", "route.hip", "decode.hip", "prefill.hip", "prefill16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for every kernel: the scalar forms

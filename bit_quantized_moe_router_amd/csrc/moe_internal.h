@@ -73,7 +73,7 @@ struct PrefillWs {
 };
 
 constexpr int kHistTokensPerBlock = 256;  // tokens per histogram block
-constexpr int kPrefillTileM = 64;         // rows per grouped-GEMM tile
+constexpr int kPrefillTileM = 64;         // rows per grouped-GEMM tile (bf16-operand path)
 
 DecodeWs decode_ws_layout(const moe_layer* L, int T);
 PrefillWs prefill_ws_layout(const moe_layer* L, int T);
@@ -90,6 +90,12 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
                   uint8_t* ws, const DecodeWs& W, uint16_t* out, void* stream, uint32_t mask);
 int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
                    uint8_t* ws, const PrefillWs& P, uint16_t* out, void* stream, uint32_t mask);
+// Prefill on exact fp16 terms (all projections ternary): the stages after routing
+// (x staging, gate/up, down), on 128-row tiles of the tile list.
+bool prefill_exact16(const moe_layer* L);
+int prefill_tile_rows(const moe_layer* L);
+int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* R, uint8_t* ws,
+                     const PrefillWs& P, void* stream, uint32_t mask);
 // out[t] = bf16([x[t]] + sum_j w[t][j] * y[inv_row[t][j]] + [y[T*k + t]]) for all T tokens
 int launch_combine(const uint16_t* y, int T, int d, int k, int n_shared, const int32_t* inv_row,
                    const float* w, const uint16_t* x, int residual, uint16_t* out, void* stream);

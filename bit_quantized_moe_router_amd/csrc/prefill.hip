@@ -410,6 +410,13 @@ int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
     const int rc = launch_route_generic(L, x, T, flags, R, ws, P, stream);
     if (rc) return rc;
   }
+  if (prefill_exact16(L)) {
+    int rc = launch_prefill16(L, x, T, R, ws, P, stream, mask);
+    if (!rc && (mask & MOE_PREFILL_STAGE_COMBINE))
+      rc = launch_combine((const uint16_t*)(ws + P.y), T, L->d, L->top_k, L->n_shared, R->inv_row,
+                          R->topk_w, x, (flags & MOE_ADD_RESIDUAL) ? 1 : 0, out, stream);
+    return rc;
+  }
   hipStream_t s = (hipStream_t)stream;
   const int k = L->top_k, d = L->d, I = L->inter;
   const int Tk = T * k;

@@ -1,0 +1,349 @@
+// Prefill on exact fp16 terms, for layers whose three projections hold
+// ternary codes (the code families of the "Xolotl" README's "Quick start";
+// the value of a code is scale * (u - offset), see include/moe.h).
+//
+// The group scale goes into the matrix-core operand instead of a per-group
+// fp32 multiply of the partial sums: a ternary weight s * (u - 1) is 0 or
+// +-s, exact in fp16.  The activations are fp16 copies of the bf16 rows
+// scaled by a power of two per row (exact in fp16's range; the epilogue
+// undoes the scale).  Each product is then exact and the matrix core
+// accumulates the whole of K in fp32: no correction term and no per-group
+// FMA, so the vector ALU only builds the operands.  A wave covers 128 rows
+// (four 32-row tiles) of its columns, so one operand build feeds four
+// matrix-core ops.  (2-bit codes split the same way into two exact terms,
+// +-s and +-s/2, which doubles the matrix-core work; measured slower than
+// the bf16-operand kernel, so they stay there.)
+//
+// A block takes one 128-row tile of one expert (tiles of this height come
+// from the routing's tile list for such layers) and one group of output
+// columns, with 4 waves:
+//   gate/up: wave w covers columns [32 (4c + w), +32) of gate and of up;
+//   down:    wave w covers columns [64 (4c + w), +64) (two column tiles).
+// Per 128-wide k-block the block stages the 128 rows' fp16 activations in
+// LDS with direct global->LDS loads (double-buffered), and each wave reads
+// its packed tiles straight into registers one k-block ahead.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace bqmoe {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRows16 = 128;                  // rows per tile
+constexpr int kCol16 = kRows16 * 16;          // one 16-byte chunk column of the tile
+constexpr int kBuf16 = kRows16 * 256;         // one k-block of activations
+constexpr int kDma16 = 16 * kRows16 / 64;     // direct loads per k-block (64 lanes x 16 B each)
+
+__device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// SiLU with the hardware exp2 and reciprocal (h is rounded to bf16 right after)
+__device__ __forceinline__ float silu16(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+// ------------------------------------------------------------ operand build
+// A lane's 32-bit code word holds two 32-groups' 8 levels each: group P
+// (0 or 1) in bits 8P .. 8P+7 (levels k = 0, 2, 4, 6 of the lane's eight) and
+// 16 + 8P .. (levels k = 1, 3, 5, 7), two bits per level, low bit first.
+// fp16 pair D (levels 2D, 2D+1) of the operand: magnitude m2 (both halves),
+// sign set where bit B of the level is clear (nw = ~word).
+template <int P, int D, int B>
+__device__ __forceinline__ uint32_t sign_pair(uint32_t nw, uint32_t m2) {
+  constexpr int pos = 8 * P + 2 * D + B;  // the bit in the low half; the high half is +16
+  return ((nw << (15 - pos)) & 0x80008000u) | m2;
+}
+
+// ternary: u = 2 b1 + b0 in {0, 1, 2} -> -s, 0, +s (a level with b0 set is 0)
+template <int P, int D>
+__device__ __forceinline__ uint32_t tern_pair(uint32_t nw, uint32_t s2) {
+  const uint32_t v = sign_pair<P, D, 1>(nw, s2);
+  const uint32_t nz = (nw >> (8 * P + 2 * D)) & 0x00010001u;  // 1 where b0 is clear
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v) * __builtin_bit_cast(u16x2, nz));
+}
+
+// The operand of one (group P of the word, k-half) of a lane.
+template <int P>
+__device__ __forceinline__ u32x4 build_tern(uint32_t word, uint32_t s2) {
+  const uint32_t nw = ~word;
+  return u32x4{tern_pair<P, 0>(nw, s2), tern_pair<P, 1>(nw, s2), tern_pair<P, 2>(nw, s2),
+               tern_pair<P, 3>(nw, s2)};
+}
+
+// ------------------------------------------------------------------ staging
+// One wave per row of bf16 values: e = max(0, exponent of max|v| - 14), so
+// that every |v| * 2^-e < 2^15; dst = fp16(v * 2^-e) (exact for the row's
+// values down to 2^-17 of its maximum, rounded to nearest below), scale =
+// 2^e.  src and dst may be the same rows (each lane rewrites what it read).
+__global__ __launch_bounds__(256) void k_stage16(const uint16_t* src, int rows, int K,
+                                                 uint16_t* dst, float* __restrict__ scale) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const uint16_t* s = src + (size_t)row * K;
+  uint16_t* d = dst + (size_t)row * K;
+  uint32_t m = 0;
+  for (int i = lane * 8; i < K; i += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(s + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  const int e = max(0, (int)(m >> 7) - 127 - 14);
+  const float f = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e <= 114
+  for (int i = lane * 8; i < K; i += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(s + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = (_Float16)(bf16_to_f32(w[j] & 0xFFFFu) * f);
+      const _Float16 hi = (_Float16)(bf16_to_f32(w[j] >> 16) * f);
+      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(d + i) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (lane == 0) scale[row] = __uint_as_float((uint32_t)(127 + e) << 23);
+}
+
+// ------------------------------------------------------------- grouped GEMM
+// NMAT = 2: gate (column tile 0) and up (column tile 1); NMAT = 1: down (two
+// column tiles).  A: fp16 rows (gather: tile row -> token through perm_tok),
+// rscale: 2^e of each source row.
+template <int NMAT>
+__global__ __launch_bounds__(256, 2) void k_pf16(
+    const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
+    ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ tiles, const int32_t* __restrict__ ctrl,
+    const int32_t* __restrict__ perm_tok, int Tk, int gather, const uint16_t* __restrict__ A,
+    const float* __restrict__ rscale, int K, int N, uint16_t* __restrict__ out, int ncol) {
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * kBuf16];
+  __shared__ int sTok[kRows16];
+  __shared__ float sScale[kRows16];
+
+  // work item = (row tile, column group), tile-major; each XCD takes one
+  // contiguous chunk of the items (blocks go to the 8 XCDs round-robin), so
+  // the column groups of a row tile share its activations in one L2
+  const int n_items = ctrl[0] * ncol;
+  const int chunk = (n_items + 7) / 8;
+  const int local = blockIdx.x / 8;
+  const int item = (blockIdx.x % 8) * chunk + local;
+  if (local >= chunk || item >= n_items) return;
+  const int tile = item / ncol, col = item % ncol;
+  const int32_t* tl = tiles + 4 * tile;
+  const int e = tl[0], row0 = tl[1], M = tl[2];
+  const uint8_t* blob = e >= 0 ? experts + (size_t)e * stride : shared;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hl = lane >> 5, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KB = K / 128;
+
+  // source row of each tile row; padding rows repeat the first row (never stored)
+  if (tid < kRows16) {
+    const int row = row0 + (tid < M ? tid : 0);
+    const int src = gather ? (row < Tk ? perm_tok[row] : row - Tk) : row;
+    sTok[tid] = src;
+    sScale[tid] = rscale[src];
+  }
+  __syncthreads();
+  const uint16_t* arow[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) arow[h] = A + (size_t)sTok[64 * h + lane] * K;
+
+  const int cw = col * 4 + wave;
+  const uint8_t* const base0 = blob + pa.off;
+  const uint8_t* const base1 = blob + pb.off;
+  const size_t scl0 = pa.scales, scl1 = pb.scales;
+  int ntl[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) ntl[ct] = (NMAT == 2 ? cw * 2 : cw * 4 + 2 * ct) + (l32 >> 4);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rt][ct][i] = 0.f;
+
+  // packed tiles of the k-block in use (c*) and of the next one (n*): per
+  // column tile the lane's two 8-B code chunks and its column's 4 scales
+  u32x2 cw_[2][2], cs_[2], nw_[2][2], ns_[2];
+
+  // chunk column c (8 k) of row R at c * kCol16 + R * 16: 32 rows of one
+  // matrix-core read are 512 contiguous bytes
+#define BQ16_ISSUE(KB_, BUF_)                                                                  \
+  {                                                                                            \
+    uint8_t* dst = sbuf + (BUF_) * kBuf16;                                                     \
+    _Pragma("unroll") for (int i = 0; i < kDma16 / 4; ++i) {                                   \
+      const int ci = wave * (kDma16 / 4) + i; /* chunk column ci / 2, rows 64 (ci % 2) .. */   \
+      const uint16_t* src = arow[ci % 2] + (KB_) * 128 + (ci / 2) * 8;                         \
+      __builtin_amdgcn_global_load_lds((const void*)src,                                       \
+                                       (lds_void*)(dst + (ci / 2) * kCol16 + (ci % 2) * 1024), \
+                                       16, 0, 0);                                              \
+    }                                                                                          \
+  }
+#define BQ16_LOADB(KB_, W_, S_)                                                                \
+  {                                                                                            \
+    _Pragma("unroll") for (int ct = 0; ct < 2; ++ct) {                                         \
+      const bool sec = NMAT == 2 && ct == 1;                                                   \
+      const uint8_t* bb = sec ? base1 : base0;                                                 \
+      const size_t tile_ = (size_t)ntl[ct] * KB + (KB_);                                       \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h) W_[ct][h] =                                \
+          *reinterpret_cast<const u32x2*>(bb + tile_ * 512 + (16 * (2 * h + hl) + r) * 8);    \
+      S_[ct] = *reinterpret_cast<const u32x2*>(bb + (sec ? scl1 : scl0) + tile_ * 128 + r * 8); \
+    }                                                                                          \
+  }
+
+  BQ16_ISSUE(0, 0)
+  BQ16_LOADB(0, cw_, cs_)
+  for (int kb = 0; kb < KB; ++kb) {
+    const int buf = kb & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // k-block kb is in LDS for every wave; buffer buf^1 is free
+    if (kb + 1 < KB) {
+      BQ16_ISSUE(kb + 1, buf ^ 1)
+      BQ16_LOADB(kb + 1, nw_, ns_)
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* sA = sbuf + buf * kBuf16;
+
+    // A fragments of group GB (8 reads of 16 B per lane)
+#define BQ16_READA(DST, GB)                                                                     \
+  _Pragma("unroll") for (int rt = 0; rt < 4; ++rt)                                              \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h) DST[rt][h] =                                \
+          *reinterpret_cast<const u32x4*>(sA + ((GB) * 4 + 2 * h + hl) * kCol16 +              \
+                                          (rt * 32 + l32) * 16);
+    // group GB on the fragments in aa; the next group's are read first, so
+    // that their LDS latency runs under this group's matrix-core ops
+#define BQ16_GROUP(GB)                                                                          \
+  {                                                                                             \
+    if constexpr ((GB) < 3) { BQ16_READA(an, (GB) + 1) }                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
+    uint32_t s2[2];                                                                             \
+    _Pragma("unroll") for (int ct = 0; ct < 2; ++ct) {                                          \
+      /* fp16 scale of (column l32, group GB), in both halves */                                \
+      const uint32_t sh = ((((GB) < 2) ? cs_[ct][0] : cs_[ct][1]) >> (16 * ((GB) & 1))) & 0xFFFFu; \
+      s2[ct] = sh | (sh << 16);                                                                 \
+    }                                                                                           \
+    /* per k-half: both column tiles' operands, then 8 independent ops */                       \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                             \
+      u32x4 t[2];                                                                               \
+      _Pragma("unroll") for (int ct = 0; ct < 2; ++ct)                                          \
+          t[ct] = build_tern<(GB) & 1>(((GB) < 2) ? cw_[ct][h][0] : cw_[ct][h][1], s2[ct]);     \
+      _Pragma("unroll") for (int rt = 0; rt < 4; ++rt)                                          \
+          _Pragma("unroll") for (int ct = 0; ct < 2; ++ct)                                      \
+              acc[rt][ct] = mfma_f16(aa[rt][h], t[ct], acc[rt][ct]);                            \
+    }                                                                                           \
+    if constexpr ((GB) < 3) {                                                                   \
+      _Pragma("unroll") for (int rt = 0; rt < 4; ++rt)                                          \
+          _Pragma("unroll") for (int h = 0; h < 2; ++h) aa[rt][h] = an[rt][h];                  \
+    }                                                                                           \
+  }
+    u32x4 aa[4][2], an[4][2];
+    BQ16_READA(aa, 0)
+    BQ16_GROUP(0)
+    BQ16_GROUP(1)
+    BQ16_GROUP(2)
+    BQ16_GROUP(3)
+#undef BQ16_GROUP
+#undef BQ16_READA
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      cs_[ct] = ns_[ct];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) cw_[ct][h] = nw_[ct][h];
+    }
+  }
+#undef BQ16_ISSUE
+#undef BQ16_LOADB
+
+  // acc[rt][ct][i] is row rt*32 + 8(i/4) + 4(lane/32) + i%4, column l32 of
+  // column tile ct; the row's 2^e undoes the activation scale
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = rt * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+      if (m < M) {
+        const float sc = sScale[m];
+        if constexpr (NMAT == 2) {
+          // gate and up of the same column of I: h = bf16(SiLU(g) * u)
+          const float g = acc[rt][0][i] * sc, u = acc[rt][1][i] * sc;
+          out[(size_t)(row0 + m) * N + cw * 32 + l32] = (uint16_t)f32_to_bf16(silu16(g) * u);
+        } else {
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+            out[(size_t)(row0 + m) * N + cw * 64 + ct * 32 + l32] =
+                (uint16_t)f32_to_bf16(acc[rt][ct][i] * sc);
+        }
+      }
+    }
+}
+
+// --------------------------------------------------------------- launchers
+bool prefill_exact16(const moe_layer* L) {
+  return L->q_gate == MOE_Q_TERNARY && L->q_up == MOE_Q_TERNARY && L->q_down == MOE_Q_TERNARY;
+}
+
+int prefill_tile_rows(const moe_layer* L) { return prefill_exact16(L) ? kRows16 : kPrefillTileM; }
+
+static ProjDesc proj16(const moe_layer* L, int m) {
+  const int K = m < 2 ? L->d : L->inter, N = m < 2 ? L->inter : L->d;
+  const PackedLayout lt = packed_layout(MOE_Q_TERNARY, L->d, L->inter);
+  const PackedLayout me = packed_layout(MOE_Q_TERNARY, K, N);
+  ProjDesc p{};
+  p.off = (size_t)m * lt.total;
+  p.plane1 = me.plane1;
+  p.scales = me.scales;
+  p.qtype = MOE_Q_TERNARY;
+  p.K = K;
+  p.N = N;
+  return p;
+}
+
+// The workspace areas of the bf16-operand path hold, here: xs the fp16 rows
+// of x, xsum their scales; h the bf16 h and then its fp16 rows, hsum their
+// scales.
+int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* R, uint8_t* ws,
+                     const PrefillWs& P, void* stream, uint32_t mask) {
+  hipStream_t s = (hipStream_t)stream;
+  const int k = L->top_k, d = L->d, I = L->inter;
+  const int Tk = T * k;
+  const int rows = Tk + (L->n_shared ? T : 0);
+  uint16_t* xs = (uint16_t*)(ws + P.xs);
+  float* xscale = (float*)(ws + P.xsum);
+  uint16_t* hs = (uint16_t*)(ws + P.h);
+  float* hscale = (float*)(ws + P.hsum);
+  uint16_t* y = (uint16_t*)(ws + P.y);
+  const int32_t* tiles = (const int32_t*)(ws + P.tiles);
+  const int32_t* ctrl = (const int32_t*)(ws + P.ctrl);
+  const uint8_t* experts = (const uint8_t*)L->experts;
+  const uint8_t* shared = (const uint8_t*)L->shared;
+  if (mask & MOE_PREFILL_STAGE_STAGE_X)
+    hipLaunchKernelGGL(k_stage16, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, xs, xscale);
+  // grids: every (row tile, column group) item of the largest possible tile list
+  if (mask & MOE_PREFILL_STAGE_GATEUP) {
+    const dim3 g1((unsigned)(((long)P.max_tiles * (I / 128) + 7) / 8 * 8));
+    hipLaunchKernelGGL(k_pf16<2>, g1, dim3(256), 0, s, experts, L->expert_stride, shared,
+                       proj16(L, 0), proj16(L, 1), tiles, ctrl, R->perm_tok, Tk, 1, xs, xscale, d,
+                       I, hs, I / 128);
+  }
+  if (mask & MOE_PREFILL_STAGE_DOWN) {
+    hipLaunchKernelGGL(k_stage16, dim3((rows + 3) / 4), dim3(256), 0, s, hs, rows, I, hs, hscale);
+    const dim3 g2((unsigned)(((long)P.max_tiles * (d / 256) + 7) / 8 * 8));
+    const ProjDesc pdn = proj16(L, 2);
+    hipLaunchKernelGGL(k_pf16<1>, g2, dim3(256), 0, s, experts, L->expert_stride, shared, pdn,
+                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hscale, I, d, y, d / 256);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace bqmoe

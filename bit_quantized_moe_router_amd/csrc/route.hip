@@ -356,10 +356,11 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ ids, i
 }
 
 // Single block: per-expert exclusive scan over blocks (in place), counts,
-// offsets, and the grouped-GEMM tile list (routed experts in id order, then
+// offsets, and the grouped-GEMM tile list of tm-row tiles (routed experts in id order, then
 // the shared expert).
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nblk, int E, int T,
-                                               int k, int n_shared, int32_t* __restrict__ counts,
+                                               int k, int n_shared, int tm,
+                                               int32_t* __restrict__ counts,
                                                int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ tiles,
                                                int32_t* __restrict__ ctrl) {
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
     }
     s_cnt[e] = run;
     s_off[e] = run;
-    s_nt[e] = (run + kPrefillTileM - 1) / kPrefillTileM;
+    s_nt[e] = (run + tm - 1) / tm;
   }
   __syncthreads();
   const int total = block_exclusive_scan(s_off, E, s_tot);
@@ -386,23 +387,23 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   for (int e = tid; e < E; e += blockDim.x) {
     counts[e] = s_cnt[e];
     offsets[e] = s_off[e];
-    const int n = (s_cnt[e] + kPrefillTileM - 1) / kPrefillTileM;
+    const int n = (s_cnt[e] + tm - 1) / tm;
     for (int i = 0; i < n; ++i) {
       int32_t* t = tiles + 4 * (s_nt[e] + i);
       t[0] = e;
-      t[1] = s_off[e] + i * kPrefillTileM;
-      t[2] = min(kPrefillTileM, s_cnt[e] - i * kPrefillTileM);
+      t[1] = s_off[e] + i * tm;
+      t[2] = min(tm, s_cnt[e] - i * tm);
       t[3] = 0;
     }
   }
   int nsh = 0;
   if (n_shared) {
-    nsh = (T + kPrefillTileM - 1) / kPrefillTileM;
+    nsh = (T + tm - 1) / tm;
     for (int i = tid; i < nsh; i += blockDim.x) {
       int32_t* t = tiles + 4 * (ntiles + i);
       t[0] = -1;
-      t[1] = T * k + i * kPrefillTileM;
-      t[2] = min(kPrefillTileM, T - i * kPrefillTileM);
+      t[1] = T * k + i * tm;
+      t[2] = min(tm, T - i * tm);
       t[3] = 0;
     }
   }
@@ -456,6 +457,7 @@ int launch_route_generic(const moe_layer* L, const uint16_t* x, int T, uint32_t 
   int32_t* lrank = (int32_t*)(ws + P.lrank);
   hipLaunchKernelGGL(k_hist, dim3(P.nblk), dim3(256), 0, s, R->topk_ids, T, E, k, hist, lrank);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, P.nblk, E, T, k, L->n_shared,
+                     prefill_tile_rows(L),
                      R->counts, R->offsets, (int32_t*)(ws + P.tiles), (int32_t*)(ws + P.ctrl));
   hipLaunchKernelGGL(k_scatter, dim3((T * k + 255) / 256), dim3(256), 0, s, R->topk_ids, T, E, k,
                      hist, R->offsets, lrank, R->perm_tok, R->inv_row);
