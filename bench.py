@@ -13,6 +13,12 @@ Default run (prints one JSON line):
   * prefill, 8192 tokens (logits given): tokens/s of the full layer call and
     the grouped GEMMs' matrix-core utilisation (useful flops / GEMM time /
     2.5 PFLOP/s).
+  * decode_kernels: packed expert bytes / (gate/up + down kernel time), the
+    kernels' HBM figure; us_per_layer_warm: the same layer and token every
+    step (experts cached), for reference only.
+  * ceilings: measured on the box (libbqceil.so) -- the best single-launch HBM
+    read rate at the kernels' byte counts and dense bf16 matrix-core TFLOP/s;
+    each kernel figure is also given as a fraction of these.
   * cpu_baseline: the CPU oracle on a bounded sample of decode tokens.
 """
 from __future__ import annotations
@@ -81,6 +87,8 @@ def parse():
                     help="further workloads measured after the headline ones and reported in "
                          "the same line: c2 (decode, 8 tokens), c4 (4-layer prefill stack); "
                          "'none' skips them")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured roofline ceilings (read stream, matrix-core peak)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="profiling aid: run only the prefill leg and print its result")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -172,28 +180,110 @@ def decode_leg(args, dev):
     # back-to-back launches between one pair of events on the launch stream:
     # the average includes the short gap between consecutive kernels
     reps = max(K, 8 * C)
-    for r in range(C):
-        bq.moe_forward_decode_stages(handles[r], xd[r], T, 0, Rs[r], wss[r], outs[r], GU)
-    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a_ev.record()
-    for r in range(reps):
-        j = r % C
-        bq.moe_forward_decode_stages(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j], GU)
-    b_ev.record()
-    torch.cuda.synchronize()
-    gu_us = a_ev.elapsed_time(b_ev) * 1e3 / reps
+
+    def stage_us(stage):
+        for r in range(C):
+            bq.moe_forward_decode_stages(handles[r], xd[r], T, 0, Rs[r], wss[r], outs[r], stage)
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a_ev.record()
+        for r in range(reps):
+            j = r % C
+            bq.moe_forward_decode_stages(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j], stage)
+        b_ev.record()
+        torch.cuda.synchronize()
+        return a_ev.elapsed_time(b_ev) * 1e3 / reps
+
+    gu_us = stage_us(GU)
+    # the down projection (+ combine) re-runs on each copy's h from the gate/up runs above
+    dn_us = stage_us(bq.MOE_DECODE_STAGE_DOWN)
     gu_b = float(np.mean([gu_bytes[r % C] for r in range(reps)]))
+    exp_b = float(np.mean([
+        (int((Rs[r % C].counts > 0).sum().item()) + cfg.n_shared) * ebytes for r in range(C)]))
+
+    # warm: the same layer copy and token every step (its experts stay in the
+    # last-level cache), K steps as one graph
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for i in range(K):
+            step(W)
+    gw.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    gw.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / K
     traffic = measured_traffic("k_dec_gateup")
     roof = {"kernel": "k_dec_gateup (decode gate/up + SiLU)", "bound": "hbm",
             "achieved": gu_b / (gu_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
             "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_b}
-    res = dict(cfg=cfg, ms=ms, eager_ms=eager_ms, bytes_per_step=bytes_per_step,
-               router_bytes=router_bytes, roof=roof, active=float(np.mean(active)))
-    del g, experts, shared, handles
+    kernels = {"gateup_us": gu_us, "down_us": dn_us, "packed_expert_bytes": exp_b,
+               "gbs": exp_b / ((gu_us + dn_us) * 1e-6) / 1e9,
+               "frac": exp_b / ((gu_us + dn_us) * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    res = dict(cfg=cfg, ms=ms, eager_ms=eager_ms, warm_ms=warm_ms, bytes_per_step=bytes_per_step,
+               router_bytes=router_bytes, roof=roof, kernels=kernels,
+               active=float(np.mean(active)))
+    del g, gw, experts, shared, handles
     torch.cuda.empty_cache()
     return res
+
+
+def ceilings_leg(dev, sizes):
+    """Measured roofline ceilings (libbqceil.so): the best single-launch HBM read
+    rate for each size over a few launch shapes (rotating over 2 GiB so the
+    last-level cache holds none of it), and dense bf16 matrix-core TFLOP/s."""
+    import ctypes
+
+    import torch
+
+    from bit_quantized_moe_router_amd import build as B
+
+    lib = ctypes.CDLL(B.CEIL_LIB)
+    lib.bqc_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.bqc_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bqc_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.bqc_mfma_bf16_flops.restype = ctypes.c_double
+    stream = torch.cuda.current_stream().cuda_stream
+    span = 256 << 20
+    buf = torch.ones(8 * span, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    base = buf.data_ptr()
+    reps = 24
+
+    def timed(launch):
+        launch(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for r in range(reps):
+            launch(r)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms
+
+    read = {}
+    for n in sizes:
+        best = None
+        for blocks, unroll in ((512, 4), (1024, 2), (1024, 4), (2048, 1)):
+            def launch(r, n=n, blocks=blocks, unroll=unroll):
+                assert lib.bqc_read_stream(base + (r % 8) * span, n, blocks, unroll,
+                                           sink.data_ptr(), stream) == 0
+            ms = timed(launch)
+            best = ms if best is None or ms < best else best
+        read[str(n)] = {"us": best * 1e3, "gbs": n / (best * 1e-3) / 1e9}
+    blocks, iters = 1024, 2000
+
+    def mlaunch(r):
+        assert lib.bqc_mfma_bf16(blocks, iters, sink.data_ptr(), stream) == 0
+    ms = timed(mlaunch)
+    tflops = lib.bqc_mfma_bf16_flops(blocks, iters) / (ms * 1e-3) / 1e12
+    del buf
+    torch.cuda.empty_cache()
+    return {"hbm_read": read, "mfma_bf16_tflops": tflops,
+            "note": "single launches, best of 4 launch shapes; spec peaks 8000 GB/s, 2500 TFLOP/s"}
 
 
 def prefill_leg(args, dev):
@@ -343,6 +433,20 @@ def main():
     pre = None if args.prefill_config == "none" else prefill_leg(args, dev)
     extra = extra_legs(args, dev)
     cfg = d["cfg"]
+    kern = d["kernels"]
+    ceil = None
+    if not args.no_ceilings:
+        ceil = ceilings_leg(dev, [int(d["roof"]["algorithmic_bytes_per_launch"]),
+                                  int(kern["packed_expert_bytes"]), 256 << 20])
+        c_gu = ceil["hbm_read"][str(int(d["roof"]["algorithmic_bytes_per_launch"]))]["gbs"]
+        c_all = ceil["hbm_read"][str(int(kern["packed_expert_bytes"]))]["gbs"]
+        d["roof"]["ceiling_gbs"] = c_gu
+        d["roof"]["frac_of_ceiling"] = d["roof"]["achieved"] / c_gu
+        kern["ceiling_gbs"] = c_all
+        kern["frac_of_ceiling"] = kern["gbs"] / c_all
+        for leg in (pre, extra.get("prefill_c4")):
+            if leg:
+                leg["mfma_frac_of_ceiling"] = leg["mfma_frac"] * BF16_PEAK_TFLOPS / ceil["mfma_bf16_tflops"]
     cpu = cpu_baseline(args, cfg, d["bytes_per_step"]) if args.cpu_seconds > 0 else None
     gbs = d["bytes_per_step"] / (d["ms"] * 1e-3) / 1e9
     line = {
@@ -364,12 +468,15 @@ def main():
                    "step": "one full decode layer call (fresh token, next layer copy)"},
         "us_per_layer": d["ms"] * 1e3,
         "us_per_layer_eager": d["eager_ms"] * 1e3,
+        "us_per_layer_warm": d["warm_ms"] * 1e3,
+        "decode_kernels": kern,
         "packed_expert_bytes_per_step": d["bytes_per_step"],
         "active_experts_per_step": d["active"],
         "gbs_incl_router": (d["bytes_per_step"] + d["router_bytes"]) / (d["ms"] * 1e-3) / 1e9,
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "roofline": d["roof"],
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "prefill": pre,
         **extra,
     }
@@ -392,7 +499,8 @@ def extra_legs(args, dev):
             "unique_routed_experts_per_step": d["active"] - d["cfg"].n_shared,
             "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "gateup_kernel_us": d["roof"]["avg_launch_us"],
-            "gateup_kernel_gbs": d["roof"]["achieved"]}
+            "gateup_kernel_gbs": d["roof"]["achieved"],
+            "decode_kernels": d["kernels"]}
     if "c4" in want:
         a = argparse.Namespace(**vars(args))
         a.prefill_config, a.prefill_steps = "c4", 2

@@ -1,6 +1,7 @@
 """Host-side tests of the C ABI (no GPU needed).
 
-* the library loads and exports every function include/moe.h declares;
+* the library loads and exports every function include/moe.h declares, and
+  the benchmark's ceilings library every function include/ceilings.h does;
 * the host packer agrees with the oracle's independent decoder of the format
   (both written from the format definition) on every level and on special
   scales;
@@ -29,6 +30,30 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert bq.moe_abi_version() == 1
+
+
+def test_ceilings_library_exports_every_declared_symbol():
+    from bit_quantized_moe_router_amd import build as B
+
+    if not os.path.exists(B.CEIL_LIB):
+        pytest.skip("libbqceil.so not built")
+    lib = ctypes.CDLL(B.CEIL_LIB)
+    text = open(os.path.join(ROOT, "include", "ceilings.h")).read()
+    declared = set(re.findall(r"\b(bqc_[a-z0-9_]+)\s*\(", text))
+    assert declared == {"bqc_read_stream", "bqc_mfma_bf16", "bqc_mfma_bf16_flops"}
+    for name in declared:
+        assert hasattr(lib, name), name
+    # argument errors come back before any launch (no GPU needed)
+    lib.bqc_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.bqc_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bqc_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.bqc_mfma_bf16_flops.restype = ctypes.c_double
+    assert lib.bqc_read_stream(None, 1024, 8, 4, 16, None) == 1
+    assert lib.bqc_read_stream(16, 1000, 8, 4, 16, None) == 1   # not a multiple of 16
+    assert lib.bqc_read_stream(16, 1024, 8, 3, 16, None) == 1   # unsupported unroll
+    assert lib.bqc_mfma_bf16(0, 10, 16, None) == 1
+    assert lib.bqc_mfma_bf16_flops(2, 3) == 2 * 4 * 3 * 4 * 32 * 32 * 16 * 2
 
 
 def test_status_strings():
