@@ -588,7 +588,15 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
   int e, row0, M;
   uint32_t tok3 = 0;  // tokens of the slot's rows, 3 bits each
   if constexpr (ROUTE) {
-    dec_select_one_token(ro, slot, e, row0, M);
+    if (slot == ro.k && ro.n_shared) {
+      // the shared expert's blocks need no selection (slot k, permuted row k):
+      // they stream at once, under the routed blocks' top-k
+      e = -1;
+      row0 = ro.k;
+      M = 1;
+    } else {
+      dec_select_one_token(ro, slot, e, row0, M);
+    }
   } else {
     // the slot record is uniform: scalar loads, which do not wait behind the
     // packed-tile loads below; records past the last slot have M == 0
