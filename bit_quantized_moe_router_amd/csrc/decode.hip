@@ -67,11 +67,14 @@ __host__ __device__ constexpr int ring_sum_stride() { return 64 + 16; }
 __host__ __device__ constexpr int ring_bytes(int rc) {
   return rc * (ring_row_stride() + ring_sum_stride());
 }
-// LDS of one wave, rounded to 256 B, then 256 B of zeros (the A operand of
-// band rows that hold no row; see the band pipeline)
-__host__ __device__ constexpr int ring_wave_bytes(int rc) {
-  return ((ring_bytes(rc) + 255) & ~255) + 256;
+// LDS of one wave: the buffer rounded to 256 B, then 256 B of zeros (the A
+// operand of band rows that hold no row; see the band pipeline) placed 208 B
+// further, in banks that no real-row read of the same instruction uses
+// (row caps 1, 2 and 4).  Its offset in the buffer:
+__host__ __device__ constexpr int ring_zero_offset(int rc) {
+  return ((ring_bytes(rc) + 255) & ~255) + 208;
 }
+__host__ __device__ constexpr int ring_wave_bytes(int rc) { return ring_zero_offset(rc) + 256; }
 
 template <int RC>
 struct KbRegs {
@@ -341,7 +344,7 @@ __device__ __forceinline__ void dec_pipeline_bandr(
     int row0, uint32_t tok3, const uint16_t* __restrict__ A, const uint8_t* __restrict__ Asum,
     int K, u32x4 bca, u32x4 bcb, const Unpack2R& ur) {
   static_assert(MR <= 4 && RC >= MR, "band rows");
-  uint8_t* zbuf = buf + ring_wave_bytes(RC) - 256;
+  uint8_t* zbuf = buf + ring_zero_offset(RC);
   *reinterpret_cast<u32x4*>(zbuf + (lane & 15) * 16) = u32x4{0u, 0u, 0u, 0u};
   // per-lane operand addresses: lane l reads row c = l % 4 of group g = (l % 16) / 4
   const int q = lane >> 4, c = lane & 3, g = (lane >> 2) & 3;
@@ -382,10 +385,12 @@ __device__ __forceinline__ void dec_pipeline_bandr(
 // 4'. The pipeline of a single-token launch: the wave's whole slice of the
 //     row (KBW k-blocks, [KBW][256 B], then the sums [KBW][64 B]) is fetched
 //     into registers ahead of the first tiles and written to LDS once, next
-//     to a zeroed area of [KBW][256 B]; a k-block's work then only reads LDS.
+//     to a zeroed area of [KBW][256 B] (64 B further, so that the real and
+//     the zero lanes of one read use different banks); a k-block's work then
+//     only reads LDS.
 //     On return acc[j][0] of lanes 0..15 holds the wave's sum for column
 //     lane (the other elements are zero).
-__host__ __device__ constexpr int one_wave_bytes(int kbw) { return kbw * (256 + 64 + 256); }
+__host__ __device__ constexpr int one_wave_bytes(int kbw) { return kbw * (256 + 64 + 256) + 64; }
 
 template <int NS, bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KBW, int PRE, bool FULL>
 __device__ __forceinline__ void dec_pipeline_band(
@@ -414,7 +419,7 @@ __device__ __forceinline__ void dec_pipeline_band(
     dec_load_kb<NS, GATEUP, QA3, QB3, KBW, !FULL>(i, wc, wh, ws, code_base, plane1, scale_off, nt,
                                                   KB, kb0, lane);
   __builtin_amdgcn_sched_barrier(0);
-  uint8_t* zbuf = buf + KBW * (256 + 64);
+  uint8_t* zbuf = buf + KBW * (256 + 64) + 64;
 #pragma unroll
   for (int p = 0; p < NPA; ++p) {
     const int piece = (p * 64 + lane) & (KBW * 16 - 1);
