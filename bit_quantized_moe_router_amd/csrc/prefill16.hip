@@ -77,10 +77,12 @@ __device__ __forceinline__ u32x4 build_tern(uint32_t word, uint32_t s2) {
 }
 
 // ------------------------------------------------------------------ staging
-// One wave per row of bf16 values: e = max(0, exponent of max|v| - 14), so
-// that every |v| * 2^-e < 2^15; dst = fp16(v * 2^-e) (exact for the row's
-// values down to 2^-17 of its maximum, rounded to nearest below), scale =
-// 2^e.  src and dst may be the same rows (each lane rewrites what it read).
+// One wave per row of bf16 values: e = (exponent of max|v|) - 14, kept in
+// [-100, 114] so that 2^e and 2^-e are normal floats; every |v| * 2^-e is then
+// below 2^15 and, unless the row's maximum is below 2^-86, its maximum is at
+// least 2^14.  dst = fp16(v * 2^-e) (exact for the row's values down to 2^-17
+// of its maximum, rounded to nearest below), scale = 2^e.  src and dst may be
+// the same rows (each lane rewrites what it read).
 __global__ __launch_bounds__(256) void k_stage16(const uint16_t* src, int rows, int K,
                                                  uint16_t* dst, float* __restrict__ scale) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -96,8 +98,8 @@ __global__ __launch_bounds__(256) void k_stage16(const uint16_t* src, int rows, 
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-  const int e = max(0, (int)(m >> 7) - 127 - 14);
-  const float f = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e <= 114
+  const int e = min(114, max(-100, (int)(m >> 7) - 127 - 14));
+  const float f = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
   for (int i = lane * 8; i < K; i += 512) {
     const uint4 v = *reinterpret_cast<const uint4*>(s + i);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};

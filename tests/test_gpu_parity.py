@@ -141,6 +141,27 @@ def test_prefill_multitile_residual_and_skew(layers):
     _full_check(dl, x, "prefill", flags=bq.MOE_ADD_RESIDUAL, logits=logits, label="skew")
 
 
+def test_prefill_ternary_rows_beyond_fp16_range(layers):
+    # all-ternary layers take fp16 operands: each row is staged with a power-of-two scale of
+    # its own, so rows far above and far below fp16's range stay exact
+    cfg = synth.small_config(MULTI, name="tern_range", q_gate=synth.QT_TERNARY,
+                             q_up=synth.QT_TERNARY, q_down=synth.QT_TERNARY, T=200)
+    dl = layers("tern_range", cfg)
+    x = synth.gen_x(cfg).copy()
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    big, tiny = slice(0, 40), slice(40, 80)
+    xf[big] *= np.float32(2.0 ** 20)    # |x| up to ~2^22, beyond fp16's 65504
+    xf[tiny] *= np.float32(2.0 ** -30)  # |x| ~2^-30, below fp16's smallest subnormal
+    x = (xf.view(np.uint32) >> 16).astype(np.uint16)  # exact: power-of-two scaling of bf16
+    logits = synth.gen_logits(cfg)
+    print("[tern_range] prefill", flush=True)
+    out, rt = _run(dl, x, "prefill", logits=logits)
+    check_routing_exact(cfg, logits, rt)
+    ref = oracle_outputs(cfg, dl.layer, x, logits, np.arange(cfg.T), False)
+    for name, rows in (("big", big), ("tiny", tiny), ("plain", slice(80, cfg.T))):
+        assert_parity(out[rows], ref[rows], f"tern_range {name} rows")
+
+
 def test_prefill_int3_mixed(layers):
     cfg = synth.small_config(MULTI, name="int3mix", q_gate=synth.QT_INT3, q_up=synth.QT_INT2,
                              q_down=synth.QT_INT3, T=300)
