@@ -83,10 +83,10 @@ def parse():
                          "times")
     ap.add_argument("--loop-stage", default="gateup", choices=["gateup", "down"],
                     help="the stage --kernel-loop launches")
-    ap.add_argument("--extra", default="c2,c4",
+    ap.add_argument("--extra", default="c2,c2s,c4",
                     help="further workloads measured after the headline ones and reported in "
-                         "the same line: c2 (decode, 8 tokens), c4 (4-layer prefill stack); "
-                         "'none' skips them")
+                         "the same line: c2 (decode, 8 tokens), c2s (c2 through a 2-bit shadow "
+                         "of its 3-bit experts), c4 (4-layer prefill stack); 'none' skips them")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured roofline ceilings (read stream, matrix-core peak)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -108,7 +108,9 @@ def decode_leg(args, dev):
     cfg = synth.CONFIGS[args.config]
     T, K, W, C = cfg.T, args.steps, args.warmup, max(1, args.copies)
     log(f"[decode] building {cfg.name} + {C - 1} device copies")
-    base = workloads.DeviceLayer(cfg, 0, dev)
+    shadow = getattr(args, "shadow", None)
+    base = workloads.DeviceLayer(cfg, 0, dev, shadow_qtypes=shadow)
+    cfg = base.cfg  # the shadow's code families when one is built
     experts = [base.experts] + [base.experts.clone() for _ in range(C - 1)]
     shared = [base.shared] + [None if base.shared is None else base.shared.clone()
                               for _ in range(C - 1)]
@@ -501,6 +503,19 @@ def extra_legs(args, dev):
             "gateup_kernel_us": d["roof"]["avg_launch_us"],
             "gateup_kernel_gbs": d["roof"]["achieved"],
             "decode_kernels": d["kernels"]}
+    if "c2s" in want:
+        # C2 read through its fast-mode copy: the 3-bit gate/up experts re-quantised to 2-bit
+        a = argparse.Namespace(**vars(args))
+        a.config, a.steps, a.warmup, a.copies, a.kernel_loop = "c2", 50, 5, 4, 0
+        a.shadow = (2, 2, 2)
+        d = decode_leg(a, dev)
+        gbs = d["bytes_per_step"] / (d["ms"] * 1e-3) / 1e9
+        out["decode_c2_shadow"] = {
+            "workload": "c2_decode_t8_zipf, gate/up read from a 2-bit shadow of the 3-bit experts",
+            "T": d["cfg"].T, "steps": a.steps, "layer_copies": a.copies,
+            "us_per_layer": d["ms"] * 1e3, "packed_expert_bytes_per_step": d["bytes_per_step"],
+            "unique_routed_experts_per_step": d["active"] - d["cfg"].n_shared,
+            "gbs": gbs, "decode_kernels": d["kernels"]}
     if "c4" in want:
         a = argparse.Namespace(**vars(args))
         a.prefill_config, a.prefill_steps = "c4", 2

@@ -30,7 +30,7 @@ MOE_PREFILL_STAGE_ROUTE, MOE_PREFILL_STAGE_STAGE_X, MOE_PREFILL_STAGE_GATEUP, \
 MOE_PREFILL_STAGES_ALL = 31
 
 EXPORTED = ("moe_packed_bytes", "moe_expert_bytes", "moe_pack_weights", "moe_quantize_rtn",
-            "moe_workspace_bytes",
+            "moe_requantize", "moe_workspace_bytes",
             "moe_route_topk", "moe_forward_decode", "moe_forward_prefill",
             "moe_forward_decode_stages", "moe_forward_prefill_stages", "moe_status_string",
             "moe_abi_version")
@@ -82,6 +82,8 @@ def load():
     lib.moe_pack_weights.argtypes, lib.moe_pack_weights.restype = [i32, i64, i64, vp, vp, vp,
                                                                    sz], i32
     lib.moe_quantize_rtn.argtypes, lib.moe_quantize_rtn.restype = [i32, i64, i64, vp, vp, vp], i32
+    lib.moe_requantize.argtypes = [i32, i32, i64, i64, vp, sz, vp, sz]
+    lib.moe_requantize.restype = i32
     lib.moe_workspace_bytes.argtypes, lib.moe_workspace_bytes.restype = [L, ctypes.c_int32], sz
     lib.moe_route_topk.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp]
     lib.moe_forward_decode.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, vp]
@@ -160,6 +162,16 @@ def moe_quantize_rtn(qtype: int, w: np.ndarray):
     st = load().moe_quantize_rtn(qtype, K, N, _ptr(w), _ptr(codes), _ptr(scales))
     _check(st, "moe_quantize_rtn")
     return codes, scales[:, : K // 32]
+
+
+def moe_requantize(q_src: int, q_dst: int, K: int, N: int, blob: np.ndarray) -> np.ndarray:
+    """The packed projection `blob` (q_src, K x N) re-quantised to q_dst, on the host
+    (moe_requantize); returns the new packed bytes."""
+    blob = np.ascontiguousarray(blob, np.uint8)
+    out = np.zeros(moe_packed_bytes(q_dst, K, N), np.uint8)
+    st = load().moe_requantize(q_src, q_dst, K, N, _ptr(blob), blob.nbytes, _ptr(out), out.nbytes)
+    _check(st, "moe_requantize")
+    return out
 
 
 # -------------------------------------------------------------- layer

@@ -10,6 +10,7 @@
 // 0..2 of a group just above their low bits and another shift pair 3.
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "moe_internal.h"
 
@@ -151,4 +152,66 @@ extern "C" moe_status moe_pack_weights(int qtype, int64_t K, int64_t N, const ui
     }
   }
   return MOE_OK;
+}
+
+// Inverse of moe_pack_weights: the codes and scales of a packed projection.
+static moe_status unpack_weights(int qtype, int64_t K, int64_t N, const uint8_t* base,
+                                 uint8_t* codes, uint16_t* scales) {
+  const PackedLayout lay = packed_layout(qtype, K, N);
+  const int64_t NT = N / 16, KB = K / 128;
+  const int levels = qtype_levels(qtype);
+  for (int64_t nt = 0; nt < NT; ++nt) {
+    for (int64_t kb = 0; kb < KB; ++kb) {
+      const size_t tile = size_t(nt * KB + kb);
+      const uint32_t* p0 = reinterpret_cast<const uint32_t*>(base + lay.plane0 + tile * 512);
+      const uint32_t* p1 = reinterpret_cast<const uint32_t*>(base + lay.plane1 + tile * 256);
+      const uint16_t* ps = reinterpret_cast<const uint16_t*>(base + lay.scales + tile * 128);
+      for (int lane = 0; lane < 64; ++lane) {
+        const int q = lane >> 4, r = lane & 15;
+        const int64_t n = nt * 16 + r;
+        uint8_t* row = codes + n * K + kb * 128;
+        const uint32_t hi = qtype == MOE_Q_INT3 ? p1[lane] : 0u;
+        for (int gb = 0; gb < 4; ++gb) {
+          for (int s = 0; s < 8; ++s) {
+            const int half = s & 1, pair = s >> 1;
+            const int field = 4 * (gb & 1) + pair;
+            uint32_t u = (p0[lane * 2 + (gb >> 1)] >> (16 * half + 2 * field)) & 3u;
+            u |= ((hi >> plane1_bit(gb, half, pair)) & 1u) << 2;
+            if ((int)u >= levels) return MOE_ERR_BAD_CODES;
+            row[gb * 32 + q * 8 + s] = (uint8_t)u;
+          }
+        }
+      }
+      for (int r = 0; r < 16; ++r)
+        for (int gb = 0; gb < 4; ++gb)
+          scales[(nt * 16 + r) * (K / 32) + kb * 4 + gb] = ps[r * 4 + gb];
+    }
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_requantize(int q_src, int q_dst, int64_t K, int64_t N, const void* src,
+                                     size_t src_bytes, void* dst, size_t dst_bytes) {
+  if (!format_shape_ok(q_src, K, N) || !format_shape_ok(q_dst, K, N)) return MOE_ERR_UNSUPPORTED;
+  if (!src || !dst) return MOE_ERR_INVALID_ARG;
+  if (src_bytes < packed_layout(q_src, K, N).total || dst_bytes < packed_layout(q_dst, K, N).total)
+    return MOE_ERR_INVALID_ARG;
+  std::vector<uint8_t> codes(size_t(K * N));
+  std::vector<uint16_t> scales(size_t(N * (K / 32)));
+  moe_status st = unpack_weights(q_src, K, N, static_cast<const uint8_t*>(src), codes.data(),
+                                 scales.data());
+  if (st != MOE_OK) return st;
+  for (uint16_t sh : scales)
+    if ((sh & 0x7C00u) == 0x7C00u) return MOE_ERR_INVALID_ARG;  // infinite or NaN scale
+  // every weight s * (u - offset) is exact in fp32 (an 11-bit scale times a half-integer <= 3.5)
+  const double off = qtype_offset(q_src);
+  std::vector<float> w(size_t(K * N));
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k)
+      w[n * K + k] = (float)(f16_value(scales[n * (K / 32) + k / 32]) * ((double)codes[n * K + k] - off));
+  std::vector<uint8_t> codes2(size_t(K * N));
+  std::vector<uint16_t> scales2(size_t(N * (K / 32)));
+  st = moe_quantize_rtn(q_dst, K, N, w.data(), codes2.data(), scales2.data());
+  if (st != MOE_OK) return st;
+  return moe_pack_weights(q_dst, K, N, codes2.data(), scales2.data(), dst, dst_bytes);
 }

@@ -126,6 +126,23 @@ moe_status moe_pack_weights(int qtype, int64_t K, int64_t N, const uint8_t* code
 moe_status moe_quantize_rtn(int qtype, int64_t K, int64_t N, const float* w, uint8_t* codes,
                             uint16_t* scales);
 
+/* A packed projection in another code family: every weight of src (qtype
+ * q_src) is decoded to s * (u - offset), exactly, and quantised to q_dst by
+ * the rule of moe_quantize_rtn, then packed.  The "Xolotl" README's "Fast
+ * mode" section describes keeping a lower-bit copy of the largest experts
+ * and reading it instead of them when speed matters more than the last bit
+ * of fidelity; with this call a 2-bit shadow of 3-bit experts is built once
+ * on the host, and a second moe_layer pointing at the shadow blobs selects
+ * it at run time, per call (the kernels see an ordinary 2-bit layer).
+ *   src : host, src_bytes >= moe_packed_bytes(q_src, K, N)
+ *   dst : host, dst_bytes >= moe_packed_bytes(q_dst, K, N) (output)
+ * Returns MOE_ERR_UNSUPPORTED for a bad shape or qtype, MOE_ERR_BAD_CODES if
+ * src holds a level outside its alphabet, and MOE_ERR_INVALID_ARG for null
+ * pointers, short buffers, a non-finite scale in src, or a group whose new
+ * scale would exceed the largest fp16 value. */
+moe_status moe_requantize(int q_src, int q_dst, int64_t K, int64_t N, const void* src,
+                          size_t src_bytes, void* dst, size_t dst_bytes);
+
 /* ------------------------------------------------------------------ layer */
 typedef struct {
   int32_t d;          /* hidden size, multiple of 128 */

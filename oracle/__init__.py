@@ -147,7 +147,19 @@ def dequant(qtype, codes, scales):
     return W
 
 
+def requantize(q_src, q_dst, K, N, blob):
+    """Codes [N][K] and fp16 scale bits [N][K/32] of the packed projection `blob` (q_src)
+    re-quantised to q_dst: the oracle's own decoder, dequantisation (exact in fp32) and
+    round-to-nearest quantiser."""
+    codes, scales = unpack(q_src, K, N, blob)
+    w = np.ascontiguousarray(dequant(q_src, codes, scales).T)  # [N][K]
+    w32 = w.astype(np.float32)
+    assert np.array_equal(w32.astype(np.float64), w)
+    return quantize_rtn(q_dst, w32)
+
+
 # ------------------------------------------------------------------ routing
+
 def router_logits(x_bf16, Wr, bias=None):
     x = _c(x_bf16, np.uint16)
     Wr = _c(Wr, np.float32)

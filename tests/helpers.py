@@ -48,11 +48,29 @@ def check_routing_exact(cfg, logits, gpu, tokens=None):
     return ids, w, counts, offsets, perm_tok, inv_row
 
 
-def oracle_outputs(cfg, layer, x, logits, tokens, residual, seed=None, threads=8):
+def shadow_mats(source_cfg, qtypes, layer, seed=None):
+    """The oracle's own view of a shadow copy: per expert, each projection of `source_cfg`
+    whose code family differs from `qtypes` re-quantised by the oracle (its dequantiser and
+    round-to-nearest quantiser)."""
+    def mats(e):
+        out = []
+        for m in range(3):
+            c, s = synth.gen_matrix(source_cfg, layer, e, m, seed)
+            if qtypes[m] != source_cfg.qtypes[m]:
+                w = np.ascontiguousarray(oracle.dequant(source_cfg.qtypes[m], c, s).T)
+                c, s = oracle.quantize_rtn(qtypes[m], w.astype(np.float32))
+            out.append((c, s))
+        return out
+    return mats
+
+
+def oracle_outputs(cfg, layer, x, logits, tokens, residual, seed=None, threads=8, mats=None):
     """Oracle output rows for `tokens` (bf16 [len(tokens)][d]).
 
     Routing comes from the oracle on `logits`; only the experts the tokens use
     are regenerated and evaluated.  Tokens are independent given their routing.
+    `mats(e)`, if given, supplies expert e's three (codes, scales) in cfg's code
+    families instead of the synthetic generator.
     """
     tokens = np.asarray(tokens)
     ids, w = oracle.topk_softmax(logits[tokens], cfg.k)
@@ -67,12 +85,12 @@ def oracle_outputs(cfg, layer, x, logits, tokens, residual, seed=None, threads=8
     xs = x[tokens]
 
     def run(e):
-        mats = [synth.gen_matrix(cfg, layer, e, m, seed) for m in range(3)]
+        mm = mats(e) if mats else [synth.gen_matrix(cfg, layer, e, m, seed) for m in range(3)]
         if e == cfg.E:
-            _, yy = oracle.expert_rows(cfg.qtypes, mats, xs)
+            _, yy = oracle.expert_rows(cfg.qtypes, mm, xs)
             return e, None, yy
         rows = by_expert[e]
-        _, yy = oracle.expert_rows(cfg.qtypes, mats, xs[[i for i, _ in rows]])
+        _, yy = oracle.expert_rows(cfg.qtypes, mm, xs[[i for i, _ in rows]])
         return e, rows, yy
 
     work = list(by_expert) + ([cfg.E] if cfg.n_shared else [])

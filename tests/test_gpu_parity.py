@@ -15,7 +15,7 @@ import bit_quantized_moe_router_amd as bq
 import oracle
 import synth
 import workloads
-from helpers import assert_parity, check_routing_exact, oracle_outputs
+from helpers import assert_parity, check_routing_exact, oracle_outputs, shadow_mats
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def _run(dl, x_np, mode, flags=0, logits=None):
     return _host_u16(out), _routing_host(R, T, cfg.k)
 
 
-def _full_check(dl, x, mode, flags=0, logits=None, label=""):
+def _full_check(dl, x, mode, flags=0, logits=None, label="", mats=None):
     cfg = dl.cfg
     print(f"[{label}] {mode} T={x.shape[0]} cfg={cfg.name}", flush=True)
     out, rt = _run(dl, x, mode, flags, logits)
@@ -66,7 +66,8 @@ def _full_check(dl, x, mode, flags=0, logits=None, label=""):
         assert np.array_equal(rt["logits"], logits)
     check_routing_exact(cfg, used, rt)
     tokens = np.arange(x.shape[0])
-    ref = oracle_outputs(cfg, dl.layer, x, used, tokens, bool(flags & bq.MOE_ADD_RESIDUAL))
+    ref = oracle_outputs(cfg, dl.layer, x, used, tokens, bool(flags & bq.MOE_ADD_RESIDUAL),
+                         mats=mats)
     assert_parity(out, ref, f"{label} out")
     return out, rt
 
@@ -83,9 +84,12 @@ def layers():
 
     def get(name, cfg=None):
         if name not in cache:
-            cfg = cfg or synth.CONFIGS[name]
-            print(f"building layer {name} ({cfg.name})", flush=True)
-            cache[name] = workloads.DeviceLayer(cfg, 0, DEV)
+            if isinstance(cfg, workloads.DeviceLayer):
+                cache[name] = cfg
+            else:
+                cfg = cfg or synth.CONFIGS[name]
+                print(f"building layer {name} ({cfg.name})", flush=True)
+                cache[name] = workloads.DeviceLayer(cfg, 0, DEV)
         return cache[name]
 
     yield get
@@ -160,6 +164,20 @@ def test_prefill_ternary_rows_beyond_fp16_range(layers):
     ref = oracle_outputs(cfg, dl.layer, x, logits, np.arange(cfg.T), False)
     for name, rows in (("big", big), ("tiny", tiny), ("plain", slice(80, cfg.T))):
         assert_parity(out[rows], ref[rows], f"tern_range {name} rows")
+
+
+def test_shadow_of_3bit_experts(layers):
+    # the fast-mode copy: 3-bit gate/up re-quantised to 2-bit on the host, selected through
+    # its own layer handle; checked against the oracle's own re-quantisation
+    src = synth.small_config(MULTI, name="shadow_src", q_gate=synth.QT_INT3,
+                             q_up=synth.QT_INT3, q_down=synth.QT_INT2, T=300)
+    dl = layers("shadow", workloads.DeviceLayer(src, 0, DEV, shadow_qtypes=(2, 2, 2)))
+    assert dl.cfg.qtypes == (2, 2, 2) and dl.source_cfg.qtypes == (3, 3, 2)
+    mats = shadow_mats(src, dl.cfg.qtypes, 0)
+    _full_check(dl, synth.gen_x(src, T=8), "decode", logits=synth.gen_logits(src, T=8),
+                label="shadow", mats=mats)
+    _full_check(dl, synth.gen_x(src), "prefill", logits=synth.gen_logits(src), label="shadow",
+                mats=mats)
 
 
 def test_prefill_int3_mixed(layers):

@@ -7,6 +7,7 @@ layer's arithmetic.
 """
 from __future__ import annotations
 
+import dataclasses
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -22,17 +23,24 @@ def host_threads() -> int:
 
 
 def pack_expert(cfg: synth.Config, layer: int, e: int, out: np.ndarray | None = None,
-                seed: int | None = None) -> np.ndarray:
-    """Packed gate|up|down blob of expert e (e == E is the shared expert)."""
-    nbytes = bq.moe_expert_bytes(*cfg.qtypes, cfg.d, cfg.inter)
+                seed: int | None = None, qtypes=None) -> np.ndarray:
+    """Packed gate|up|down blob of expert e (e == E is the shared expert).  With `qtypes`,
+    a projection whose code family differs from cfg's is packed in cfg's family and then
+    re-quantised to the one given (moe_requantize): a lower-bit shadow copy."""
+    qt = tuple(qtypes or cfg.qtypes)
+    nbytes = bq.moe_expert_bytes(*qt, cfg.d, cfg.inter)
     if out is None:
         out = np.empty(nbytes, np.uint8)
     off = 0
     for m in range(3):
         K, N = synth.matrix_shape(cfg, m)
         c, s = synth.gen_matrix(cfg, layer, e, m, seed)
-        nb = bq.moe_packed_bytes(cfg.qtypes[m], K, N)
-        bq.moe_pack_weights(cfg.qtypes[m], c, s, out[off:off + nb])
+        nb = bq.moe_packed_bytes(qt[m], K, N)
+        if qt[m] == cfg.qtypes[m]:
+            bq.moe_pack_weights(qt[m], c, s, out[off:off + nb])
+        else:
+            src = bq.moe_pack_weights(cfg.qtypes[m], c, s)
+            out[off:off + nb] = bq.moe_requantize(cfg.qtypes[m], qt[m], K, N, src)
         off += nb
     return out
 
@@ -41,15 +49,23 @@ class DeviceLayer:
     """One layer's packed experts (+ shared expert, router, bias) in device memory."""
 
     def __init__(self, cfg: synth.Config, layer: int = 0, device="cuda", seed=None,
-                 experts_override=None):
+                 experts_override=None, shadow_qtypes=None):
+        # with shadow_qtypes, the experts of `cfg` re-quantised to those code families (a
+        # lower-bit copy selected per call through its own layer handle); self.cfg then
+        # carries the shadow's families and self.source_cfg the original ones
+        self.source_cfg = cfg
+        if shadow_qtypes is not None:
+            q = tuple(shadow_qtypes)
+            cfg = dataclasses.replace(cfg, q_gate=q[0], q_up=q[1], q_down=q[2])
         self.cfg = cfg
         self.layer = layer
         E = cfg.E
         self.stride = bq.moe_expert_bytes(*cfg.qtypes, cfg.d, cfg.inter)
         host = np.empty(E * self.stride, np.uint8)
+        src, qt = self.source_cfg, cfg.qtypes
 
         def work(e):
-            pack_expert(cfg, layer, e, host[e * self.stride:(e + 1) * self.stride], seed)
+            pack_expert(src, layer, e, host[e * self.stride:(e + 1) * self.stride], seed, qt)
 
         with ThreadPoolExecutor(host_threads()) as ex:
             list(ex.map(work, range(E)))
@@ -58,7 +74,7 @@ class DeviceLayer:
         self.experts = torch.from_numpy(host).to(device)
         self.shared = None
         if cfg.n_shared:
-            sh = pack_expert(cfg, layer, E, None, seed)
+            sh = pack_expert(src, layer, E, None, seed, qt)
             self.shared = torch.from_numpy(sh).to(device)
         self.router_w = None
         if cfg.router:
