@@ -312,8 +312,8 @@ static ProjDesc proj16(const moe_layer* L, int m) {
 }
 
 // The workspace areas of the bf16-operand path hold, here: xs the fp16 rows
-// of x, xsum their scales; h the bf16 h and then its fp16 rows, hsum their
-// scales.
+// of x, xsum their scales; h the bf16 h and then (by the end of the gate/up
+// stage) its fp16 rows, hsum their scales.
 int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* R, uint8_t* ws,
                      const PrefillWs& P, void* stream, uint32_t mask) {
   hipStream_t s = (hipStream_t)stream;
@@ -337,9 +337,10 @@ int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* 
     hipLaunchKernelGGL(k_pf16<2>, g1, dim3(256), 0, s, experts, L->expert_stride, shared,
                        proj16(L, 0), proj16(L, 1), tiles, ctrl, R->perm_tok, Tk, 1, xs, xscale, d,
                        I, hs, I / 128);
+    // h to scaled fp16 rows in place, within this stage, so that every stage can be re-run
+    hipLaunchKernelGGL(k_stage16, dim3((rows + 3) / 4), dim3(256), 0, s, hs, rows, I, hs, hscale);
   }
   if (mask & MOE_PREFILL_STAGE_DOWN) {
-    hipLaunchKernelGGL(k_stage16, dim3((rows + 3) / 4), dim3(256), 0, s, hs, rows, I, hs, hscale);
     const dim3 g2((unsigned)(((long)P.max_tiles * (d / 256) + 7) / 8 * 8));
     const ProjDesc pdn = proj16(L, 2);
     hipLaunchKernelGGL(k_pf16<1>, g2, dim3(256), 0, s, experts, L->expert_stride, shared, pdn,

@@ -206,7 +206,8 @@ moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T,
  * after the earlier stages have run on that workspace with the same inputs.
  * This is the hook used to time one kernel with events or a profiler, and
  * running the stages in order one call at a time is equivalent to the full
- * call.  For a single token and at most 256 experts, the decode gate/up stage
+ * call.  No stage overwrites what it reads, so a stage may also be run again
+ * on the same workspace with the same result.  For a single token and at most 256 experts, the decode gate/up stage
  * makes the expert selection itself, from R->logits, and writes everything
  * the select stage writes (same values). A call whose mask holds both SELECT
  * and GATEUP then launches no separate select kernel.  An empty or unknown
@@ -221,7 +222,8 @@ enum {
 enum {
   MOE_PREFILL_STAGE_ROUTE = 1u,    /* logits (unless given), top-k, permutation, tile list */
   MOE_PREFILL_STAGE_STAGE_X = 2u,  /* activation staging */
-  MOE_PREFILL_STAGE_GATEUP = 4u,   /* grouped GEMM gate/up + SiLU gating */
+  MOE_PREFILL_STAGE_GATEUP = 4u,   /* grouped GEMM gate/up + SiLU gating (all-ternary
+                                      layers: then h staged as scaled fp16 rows) */
   MOE_PREFILL_STAGE_DOWN = 8u,     /* grouped GEMM down */
   MOE_PREFILL_STAGE_COMBINE = 16u, /* unpermute + weighted combine */
   MOE_PREFILL_STAGES_ALL = 31u

@@ -246,6 +246,45 @@ def test_decode_stages_one_by_one_and_rerun(layers, name):
         assert np.array_equal(_host_u16(out), full), rep
 
 
+@pytest.mark.parametrize("q", [synth.QT_INT2, synth.QT_TERNARY])
+def test_prefill_stages_one_by_one_and_rerun(layers, q):
+    """The prefill stages run one call at a time give the full call's output bit for bit
+    (2-bit: bf16-operand kernels; ternary: fp16-operand kernels), and any stage re-run on
+    the same workspace reproduces it (no stage consumes what it reads)."""
+    cfg = synth.small_config(MULTI, name=f"pstages{q}", q_gate=q, q_up=q, q_down=q, T=260)
+    dl = layers(cfg.name, cfg)
+    x_np = synth.gen_x(cfg)
+    logits = synth.gen_logits(cfg)
+    T = cfg.T
+    x = _to_dev_u16(x_np)
+    R = bq.alloc_routing(T, cfg.E, cfg.k, DEV, logits=torch.from_numpy(logits).to(DEV))
+    ws = bq.alloc_workspace(dl.handle, T, DEV)
+    out = torch.empty((T, cfg.d), dtype=torch.int16, device=DEV)
+    fl = bq.MOE_LOGITS_GIVEN
+    print(f"[pstages q={q}] full call, then stage by stage", flush=True)
+    bq.moe_forward_prefill(dl.handle, x, T, fl, R, ws, out)
+    torch.cuda.synchronize()
+    full = _host_u16(out).copy()
+    ref = oracle_outputs(cfg, dl.layer, x_np, logits, np.arange(T), False)
+    assert_parity(full, ref, f"pstages q={q}")
+    stages = (bq.MOE_PREFILL_STAGE_ROUTE, bq.MOE_PREFILL_STAGE_STAGE_X,
+              bq.MOE_PREFILL_STAGE_GATEUP, bq.MOE_PREFILL_STAGE_DOWN,
+              bq.MOE_PREFILL_STAGE_COMBINE)
+    out.zero_()
+    for st in stages:
+        bq.moe_forward_prefill_stages(dl.handle, x, T, fl, R, ws, out, st)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host_u16(out), full)
+    for st in stages:  # each stage twice in a row
+        out.zero_()
+        for s_ in stages:
+            bq.moe_forward_prefill_stages(dl.handle, x, T, fl, R, ws, out, s_)
+            if s_ == st:
+                bq.moe_forward_prefill_stages(dl.handle, x, T, fl, R, ws, out, s_)
+        torch.cuda.synchronize()
+        assert np.array_equal(_host_u16(out), full), st
+
+
 def test_c3_prefill_full_sampled(layers):
     dl = layers("c3")
     cfg = dl.cfg
