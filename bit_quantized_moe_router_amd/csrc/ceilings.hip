@@ -1,4 +1,4 @@
-// Measured ceilings of the two rooflines the MoE layer is judged against,
+// Measured ceilings of the two rooflines the MoE layer is reported against,
 // for reporting kernel results beside the chip's spec peaks:
 //   - a plain HBM read stream (what a launch of a given size can read), and
 //   - dense bf16 matrix-core work with no memory traffic.
