@@ -49,7 +49,10 @@ class moe_layer(ctypes.Structure):
                 ("q_up", ctypes.c_int32), ("q_down", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("experts", ctypes.c_void_p), ("expert_stride", ctypes.c_size_t),
-                ("shared", ctypes.c_void_p)]
+                ("shared", ctypes.c_void_p),
+                ("alt_experts", ctypes.c_void_p), ("alt_stride", ctypes.c_size_t),
+                ("q_alt_gate", ctypes.c_int32), ("q_alt_up", ctypes.c_int32),
+                ("q_alt_down", ctypes.c_int32), ("alt_select", ctypes.c_void_p)]
 
 
 class moe_routing(ctypes.Structure):
@@ -183,11 +186,15 @@ class Layer:
 
 
 def make_layer(d, inter, n_experts, top_k, n_shared, qtypes, experts, expert_stride,
-               shared=None, router_w=None, router_bias=None) -> Layer:
+               shared=None, router_w=None, router_bias=None, alt=None) -> Layer:
+    """alt = (alt_experts, alt_stride, alt_qtypes, alt_select): a second copy of the routed
+    experts in other code families and the device byte mask [E] choosing it per expert."""
     qg, qu, qd = qtypes
+    ae, astride, aq, asel = alt if alt is not None else (None, 0, (0, 0, 0), None)
     c = moe_layer(d, inter, n_experts, top_k, n_shared, qg, qu, qd, _ptr(router_w),
-                  _ptr(router_bias), _ptr(experts), expert_stride, _ptr(shared))
-    return Layer(c, (experts, shared, router_w, router_bias))
+                  _ptr(router_bias), _ptr(experts), expert_stride, _ptr(shared),
+                  _ptr(ae), astride, aq[0], aq[1], aq[2], _ptr(asel))
+    return Layer(c, (experts, shared, router_w, router_bias, ae, asel))
 
 
 @dataclass

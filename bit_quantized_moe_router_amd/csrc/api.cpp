@@ -109,6 +109,14 @@ static moe_status check_common(const moe_layer* L, const uint16_t* x, int32_t T,
       return MOE_ERR_INVALID_ARG;
     if (L->n_shared && (!L->shared || !aligned(L->shared, 256))) return MOE_ERR_INVALID_ARG;
     if (!aligned(x, 16)) return MOE_ERR_INVALID_ARG;
+    if (L->alt_experts) {  // the second copy of the routed experts
+      const size_t ab =
+          moe_expert_bytes(L->q_alt_gate, L->q_alt_up, L->q_alt_down, L->d, L->inter);
+      if (!ab) return MOE_ERR_UNSUPPORTED;  // a code family outside the three
+      if (!L->alt_select || L->alt_stride < ab || L->alt_stride % 256 ||
+          !aligned(L->alt_experts, 256))
+        return MOE_ERR_INVALID_ARG;
+    }
   }
   if (!ws || ws_bytes < moe_workspace_bytes(L, T)) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
@@ -164,6 +172,7 @@ static moe_status prefill_impl(const moe_layer* L, const uint16_t* x, int32_t T,
   if (T == 0 && L && R) return MOE_OK;
   moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, true);
   if (st != MOE_OK) return st;
+  if (L->alt_experts) return MOE_ERR_UNSUPPORTED;  // the second expert copy is read by decode
   if (!out || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
   const size_t bytes = (size_t)T * L->d * 2;
   if (overlaps(x, bytes, out, bytes)) return MOE_ERR_INVALID_ARG;
@@ -212,4 +221,4 @@ extern "C" const char* moe_status_string(moe_status s) {
   return "unknown status";
 }
 
-extern "C" int moe_abi_version(void) { return 1; }
+extern "C" int moe_abi_version(void) { return 2; }

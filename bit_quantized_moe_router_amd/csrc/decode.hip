@@ -523,6 +523,7 @@ __device__ __forceinline__ void dec_select_one_token(const DecRoute& ro, int slo
         rec[0] = id;
         rec[1] = rank;
         rec[2] = 1;
+        rec[3] = 0;
         rec[kSlotTok] = 0;
       }
       if (lane == 0) {
@@ -531,6 +532,7 @@ __device__ __forceinline__ void dec_select_one_token(const DecRoute& ro, int slo
           rec[0] = -1;
           rec[1] = k;
           rec[2] = 1;
+          rec[3] = 0;
           rec[kSlotTok] = 0;
         }
         ro.slots[0] = k + (ro.n_shared ? 1 : 0);
@@ -560,6 +562,7 @@ __device__ __forceinline__ void dec_select_one_token(const DecRoute& ro, int slo
     rec[0] = 0;
     rec[1] = 0;
     rec[2] = 0;
+    rec[3] = 0;
   }
 }
 
@@ -571,6 +574,8 @@ __device__ __forceinline__ void dec_select_one_token(const DecRoute& ro, int slo
 //   of h are the two half sums added; epilogue y = bf16(acc).
 // ONE_ROW: launched for a single token, so every slot has M == 1 (the wave's
 // whole slice of the row is staged at once).
+// want_alt >= 0: only the slots whose record says they read the second
+// expert copy (1) or the first (0); the caller passes that copy's blobs.
 // ROUTE (single-token gate/up, E <= 256): the kernel makes the expert
 // selection itself instead of reading the slot list: wave 0 takes the token's
 // top-k from the logits (the routing kernels' own wave_topk), and the k
@@ -584,7 +589,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ slots, const uint16_t* __restrict__ A,
     const uint8_t* __restrict__ Asum, int K, int N, int Mmax, float ca, float cb,
-    uint16_t* __restrict__ out, float* __restrict__ out_psum, Unpack2K uk, DecRoute ro) {
+    uint16_t* __restrict__ out, float* __restrict__ out_psum, Unpack2K uk, DecRoute ro,
+    int want_alt) {
   constexpr int NS = GATEUP ? 2 : 4;
   static_assert(!ROUTE || (GATEUP && ONE_ROW), "selection inside single-token gate/up only");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -609,6 +615,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
     e = rec[0];
     row0 = rec[1];
     M = rec[2];
+    // with a second expert copy, the launch for one copy skips the other's slots
+    if (want_alt >= 0 && rec[3] != want_alt) M = 0;
     if (GATEUP) {
 #pragma unroll
       for (int c = 0; c < kDecMaxRows; ++c)
@@ -739,7 +747,8 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
     const uint16_t* __restrict__ hs, const uint8_t* __restrict__ hsum, int K, int N, int Mmax,
     float cd, Unpack2K uk, int T, int k, int n_shared, const int32_t* __restrict__ inv_row,
     const float* __restrict__ topk_w, const uint16_t* __restrict__ x, int residual,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, const uint8_t* __restrict__ alt_experts, size_t alt_stride,
+    ProjDesc pda) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int nwaves = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r = lane & 15;
@@ -761,7 +770,12 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine(
   const int32_t* rec = slots + kSlotRec * (1 + (wave < max_slots ? wave : 0));
   const int e = rec[0], row0 = rec[1], M = wave < max_slots ? rec[2] : 0;
   if (M > 0) {
-    const uint8_t* blob = e >= 0 ? experts + (size_t)e * stride : shared;
+    // a slot whose record says so reads the second expert copy (same down family)
+    const bool alt = rec[3] != 0;
+    if (alt) pd = pda;
+    const uint8_t* blob = e < 0 ? shared
+                          : alt ? alt_experts + (size_t)e * alt_stride
+                                : experts + (size_t)e * stride;
     const uint8_t* const code_base[2] = {blob + pd.off, blob + pd.off};
     const size_t plane1[2] = {pd.plane1, pd.plane1};
     const size_t scale_off[2] = {pd.scales, pd.scales};
@@ -919,7 +933,7 @@ template <bool GATEUP, bool QA3, bool QB3, bool SAMEC>
 static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const moe_layer* L,
                        ProjDesc pa, ProjDesc pb, const int32_t* slots, const uint16_t* A,
                        const uint8_t* Asum, int K, int N, float ca, float cb, uint16_t* out,
-                       float* psum, const DecRoute* route) {
+                       float* psum, const DecRoute* route, int want_alt) {
   const size_t lds = dec_lds_bytes(GATEUP, sh, Mmax);
   const DecRoute ro = route ? *route : DecRoute{};
 #define BQ_L(KS, KBW)                                                                         \
@@ -929,17 +943,17 @@ static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const
         hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, true, true>),        \
                            dim3(n_blocks), dim3(64 * KS), lds, s, (const uint8_t*)L->experts, \
                            L->expert_stride, (const uint8_t*)L->shared, pa, pb, slots, A,     \
-                           Asum, K, N, Mmax, ca, cb, out, psum, kUnpack2, ro);                \
+                           Asum, K, N, Mmax, ca, cb, out, psum, kUnpack2, ro, want_alt);      \
     } else if (Mmax == 1)                                                                     \
       hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, true>), dim3(n_blocks), \
                          dim3(64 * KS), lds, s, (const uint8_t*)L->experts, L->expert_stride, \
                          (const uint8_t*)L->shared, pa, pb, slots, A, Asum, K, N, Mmax, ca,   \
-                         cb, out, psum, kUnpack2, ro);                                        \
+                         cb, out, psum, kUnpack2, ro, want_alt);                              \
     else if constexpr (KS < 16)                                                               \
       hipLaunchKernelGGL((k_dec_proj<GATEUP, QA3, QB3, SAMEC, KS, KBW, false>),               \
                          dim3(n_blocks), dim3(64 * KS), lds, s, (const uint8_t*)L->experts,   \
                          L->expert_stride, (const uint8_t*)L->shared, pa, pb, slots, A, Asum, \
-                         K, N, Mmax, ca, cb, out, psum, kUnpack2, ro);                        \
+                         K, N, Mmax, ca, cb, out, psum, kUnpack2, ro, want_alt);              \
     else                                                                                      \
       return -1;                                                                              \
   } while (0)
@@ -975,9 +989,44 @@ static bool select_in_gateup(const moe_layer* L, int T) {
   return T == 1 && L->n_experts <= 256 && L->top_k <= 64;
 }
 
+// The second expert copy of L as a layer of its own (its blobs and code
+// families; the rest of L unchanged).
+static moe_layer alt_view(const moe_layer* L) {
+  moe_layer A = *L;
+  A.experts = L->alt_experts;
+  A.expert_stride = L->alt_stride;
+  A.q_gate = L->q_alt_gate;
+  A.q_up = L->q_alt_up;
+  A.q_down = L->q_alt_down;
+  return A;
+}
+
+// Gate/up of the slots of one expert copy (want_alt as in k_dec_proj).
+static int launch_gateup(const moe_layer* L, DecShape sh, int nb, int Mmax, hipStream_t s,
+                         const int32_t* slots, const uint16_t* xs, const uint8_t* xsum,
+                         uint16_t* hs, float* hsum, const DecRoute* rp, int want_alt) {
+  const int d = L->d, I = L->inter;
+  const ProjDesc pg = proj(L, 0), pu = proj(L, 1);
+  const float cg = qtype_offset(L->q_gate), cu = qtype_offset(L->q_up);
+  const bool g3 = L->q_gate == MOE_Q_INT3, u3 = L->q_up == MOE_Q_INT3;
+  const bool same = L->q_gate == L->q_up;
+#define BQ_GU(A3, B3, SC)                                                                       \
+  return launch_proj<true, A3, B3, SC>(sh, nb, Mmax, s, L, pg, pu, slots, xs, xsum, d, I, cg, \
+                                       cu, hs, hsum, rp, want_alt)
+  if (g3 && u3) BQ_GU(true, true, true);
+  if (g3) BQ_GU(true, false, false);
+  if (u3) BQ_GU(false, true, false);
+  if (same) BQ_GU(false, false, true);
+  BQ_GU(false, false, false);
+#undef BQ_GU
+}
+
 int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, moe_routing* R,
                   uint8_t* ws, const DecodeWs& W, uint16_t* out, void* stream, uint32_t mask) {
-  const bool fused_select = select_in_gateup(L, T) && (mask & MOE_DECODE_STAGE_GATEUP);
+  // with a second expert copy the selection stays in the select kernel, whose
+  // slot records say which copy each slot reads
+  const bool has_alt = L->alt_experts != nullptr;
+  const bool fused_select = select_in_gateup(L, T) && (mask & MOE_DECODE_STAGE_GATEUP) && !has_alt;
   int rc = launch_decode_route(L, x, T, flags, R, ws, W, stream,
                                fused_select ? mask & ~(uint32_t)MOE_DECODE_STAGE_SELECT : mask);
   if (rc) return rc;
@@ -990,40 +1039,31 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
   uint16_t* hs = (uint16_t*)(ws + W.hs);
   float* hsum = (float*)(ws + W.hsum);
   uint16_t* y = (uint16_t*)(ws + W.y);
+  const moe_layer La = has_alt ? alt_view(L) : *L;
   if (mask & MOE_DECODE_STAGE_GATEUP) {
-    const ProjDesc pg = proj(L, 0), pu = proj(L, 1);
     const DecShape sh = dec_shape(true, d, Mmax);
     const int nb = W.max_slots * (I / 16);
-    const float cg = qtype_offset(L->q_gate), cu = qtype_offset(L->q_up);
-    const bool g3 = L->q_gate == MOE_Q_INT3, u3 = L->q_up == MOE_Q_INT3;
-    const bool same = L->q_gate == L->q_up;
     const DecRoute route = {R->logits,   L->n_experts, k,         L->n_shared, W.max_slots,
                             R->topk_ids, R->topk_w,    R->counts, R->offsets,  R->perm_tok,
                             R->inv_row,  (int32_t*)(ws + W.slots)};
     const DecRoute* rp = fused_select ? &route : nullptr;
-#define BQ_GU(A3, B3, SC)                                                                   \
-  rc = launch_proj<true, A3, B3, SC>(sh, nb, Mmax, s, L, pg, pu, slots, xs, xsum, d, I, cg, \
-                                     cu, hs, hsum, rp)
-    if (g3 && u3)
-      BQ_GU(true, true, true);
-    else if (g3)
-      BQ_GU(true, false, false);
-    else if (u3)
-      BQ_GU(false, true, false);
-    else if (same)
-      BQ_GU(false, false, true);
-    else
-      BQ_GU(false, false, false);
-#undef BQ_GU
+    rc = launch_gateup(L, sh, nb, Mmax, s, slots, xs, xsum, hs, hsum, rp, has_alt ? 0 : -1);
     if (rc) return rc;
+    if (has_alt) {
+      rc = launch_gateup(&La, sh, nb, Mmax, s, slots, xs, xsum, hs, hsum, nullptr, 1);
+      if (rc) return rc;
+    }
   }
-  if ((mask & MOE_DECODE_STAGE_DOWN) && dc_ok(L, T, W.max_slots, Mmax)) {
-    const ProjDesc pd = proj(L, 2);
+  // the fused down + combine takes both copies when their down families agree
+  const bool fused_down = dc_ok(L, T, W.max_slots, Mmax) && (!has_alt || La.q_down == L->q_down);
+  if ((mask & MOE_DECODE_STAGE_DOWN) && fused_down) {
+    const ProjDesc pd = proj(L, 2), pda = proj(&La, 2);
     const int waves = dc_waves(T, W.max_slots), kbw = dc_kbw(I);
     const size_t lds = dc_lds_bytes(L, T, W.max_slots, Mmax);
     const float cd = qtype_offset(L->q_down);
     const uint8_t* hsb = (const uint8_t*)hsum;
     const int res = (flags & MOE_ADD_RESIDUAL) ? 1 : 0;
+    const uint8_t* alt_ex = (const uint8_t*)L->alt_experts;
 #define BQ_DC(Q3, KBW)                                                                         \
   do {                                                                                         \
     if (Mmax == 1)                                                                             \
@@ -1031,13 +1071,13 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
                          lds, s, (const uint8_t*)L->experts, L->expert_stride,                 \
                          (const uint8_t*)L->shared, pd, slots, W.max_slots, hs, hsb, I, d,     \
                          Mmax, cd, kUnpack2, T, k, L->n_shared, R->inv_row, R->topk_w, x, res, \
-                         out);                                                                 \
+                         out, alt_ex, L->alt_stride, pda);                                     \
     else                                                                                       \
       hipLaunchKernelGGL((k_dec_down_combine<Q3, KBW, false>), dim3(d / 16), dim3(64 * waves), \
                          lds, s, (const uint8_t*)L->experts, L->expert_stride,                 \
                          (const uint8_t*)L->shared, pd, slots, W.max_slots, hs, hsb, I, d,     \
                          Mmax, cd, kUnpack2, T, k, L->n_shared, R->inv_row, R->topk_w, x, res, \
-                         out);                                                                 \
+                         out, alt_ex, L->alt_stride, pda);                                     \
   } while (0)
 #define BQ_DCQ(Q3)        \
   do {                    \
@@ -1057,18 +1097,22 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
 #undef BQ_DCQ
 #undef BQ_DC
   } else if (mask & MOE_DECODE_STAGE_DOWN) {
-    const ProjDesc pd = proj(L, 2);
     const DecShape sh = dec_shape(false, I, Mmax);
     const int nb = W.max_slots * (d / 64);
-    const float cd = qtype_offset(L->q_down);
     const uint8_t* hsb = (const uint8_t*)hsum;
-    if (L->q_down == MOE_Q_INT3)
-      rc = launch_proj<false, true, true, true>(sh, nb, Mmax, s, L, pd, pd, slots, hs, hsb, I, d,
-                                                cd, cd, y, nullptr, nullptr);
-    else
-      rc = launch_proj<false, false, false, true>(sh, nb, Mmax, s, L, pd, pd, slots, hs, hsb, I,
-                                                  d, cd, cd, y, nullptr, nullptr);
-    if (rc) return rc;
+    for (int copy = 0; copy < (has_alt ? 2 : 1); ++copy) {
+      const moe_layer* Lc = copy ? &La : L;
+      const ProjDesc pd = proj(Lc, 2);
+      const float cd = qtype_offset(Lc->q_down);
+      const int want = has_alt ? copy : -1;
+      if (Lc->q_down == MOE_Q_INT3)
+        rc = launch_proj<false, true, true, true>(sh, nb, Mmax, s, Lc, pd, pd, slots, hs, hsb, I,
+                                                  d, cd, cd, y, nullptr, nullptr, want);
+      else
+        rc = launch_proj<false, false, false, true>(sh, nb, Mmax, s, Lc, pd, pd, slots, hs, hsb,
+                                                    I, d, cd, cd, y, nullptr, nullptr, want);
+      if (rc) return rc;
+    }
     rc = launch_combine(y, T, d, k, L->n_shared, R->inv_row, R->topk_w, x,
                         (flags & MOE_ADD_RESIDUAL) ? 1 : 0, out, stream);
     if (rc) return rc;

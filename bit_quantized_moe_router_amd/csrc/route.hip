@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kSelThreads) void k_dec_select(
     const float* __restrict__ logits, int T, int E, int k, int n_shared,
     int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_tok, int32_t* __restrict__ inv_row,
-    int32_t* __restrict__ slots, int max_slots) {
+    int32_t* __restrict__ slots, int max_slots, const uint8_t* __restrict__ alt_select) {
   __shared__ __attribute__((aligned(16))) int s_row[kDecodeMaxRoutedRows];  // expert of row t*k + j
   __shared__ int s_nact;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -255,6 +255,7 @@ __global__ __launch_bounds__(kSelThreads) void k_dec_select(
         rec[0] = id;
         rec[1] = off;
         rec[2] = __popcll(eq);
+        rec[3] = alt_select && alt_select[id] ? 1 : 0;  // read from the second expert copy
       }
     }
     if (n_shared && lane < T) {  // shared slot: rows T*k + t, token t
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(kSelThreads) void k_dec_select(
         rec[0] = -1;
         rec[1] = rows;
         rec[2] = T;
+        rec[3] = 0;
       }
       rec[kSlotTok + lane] = lane;
     }
@@ -301,6 +303,7 @@ __global__ __launch_bounds__(kSelThreads) void k_dec_select(
     rec[0] = 0;
     rec[1] = 0;
     rec[2] = 0;
+    rec[3] = 0;
   }
 }
 
@@ -490,7 +493,8 @@ int launch_decode_route(const moe_layer* L, const uint16_t* x, int T, uint32_t f
 #define BQ_SEL(PER)                                                                               \
   hipLaunchKernelGGL(k_dec_select<PER>, dim3(1), dim3(kSelThreads), 0, s, R->logits, T, E, k,    \
                      L->n_shared, R->topk_ids, R->topk_w, R->counts, R->offsets, R->perm_tok,    \
-                     R->inv_row, (int32_t*)(ws + W.slots), W.max_slots)
+                     R->inv_row, (int32_t*)(ws + W.slots), W.max_slots,                          \
+                     L->alt_experts ? L->alt_select : nullptr)
     if (E <= 64)
       BQ_SEL(1);
     else if (E <= 128)

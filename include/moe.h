@@ -158,6 +158,22 @@ typedef struct {
                                256-B aligned (gate | up | down, see moe_expert_bytes) */
   size_t expert_stride;     /* >= moe_expert_bytes(...), multiple of 256 */
   const void* shared;       /* device packed shared expert (same layout), or NULL if none */
+  /* Per-expert mixed precision (decode).  The "Xolotl" README's "Fast mode"
+   * section keeps a lower-bit copy of the largest experts and reads it in
+   * their place.  Here a second copy of the routed experts may be given in
+   * other code families; alt_select picks, per expert, the copy that decode
+   * calls read.  alt_experts == NULL: no second copy (the fields below are
+   * then ignored).  Prefill calls on a layer with a second copy return
+   * MOE_ERR_UNSUPPORTED.  The shared expert always comes from `shared`.
+   * Errors: an unknown q_alt_* gives MOE_ERR_UNSUPPORTED; a NULL alt_select,
+   * a short or unaligned alt_stride or an unaligned alt_experts gives
+   * MOE_ERR_INVALID_ARG. */
+  const void* alt_experts;  /* device: expert e's blob at alt_experts + e*alt_stride,
+                               in the families q_alt_* (layout as `experts`) */
+  size_t alt_stride;        /* >= moe_expert_bytes(q_alt_*), multiple of 256 */
+  int32_t q_alt_gate, q_alt_up, q_alt_down;
+  const uint8_t* alt_select; /* device [n_experts]: nonzero = expert e is read from the
+                                second copy */
 } moe_layer;
 
 typedef struct {           /* caller-allocated device buffers, written by the calls below */
@@ -207,7 +223,8 @@ moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T,
  * This is the hook used to time one kernel with events or a profiler, and
  * running the stages in order one call at a time is equivalent to the full
  * call.  No stage overwrites what it reads, so a stage may also be run again
- * on the same workspace with the same result.  For a single token and at most 256 experts, the decode gate/up stage
+ * on the same workspace with the same result.  For a single token, at most
+ * 256 experts and no second expert copy, the decode gate/up stage
  * makes the expert selection itself, from R->logits, and writes everything
  * the select stage writes (same values). A call whose mask holds both SELECT
  * and GATEUP then launches no separate select kernel.  An empty or unknown
@@ -238,7 +255,7 @@ moe_status moe_forward_prefill_stages(const moe_layer* L, const uint16_t* x, int
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (2 added the second expert copy to moe_layer). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -64,13 +64,15 @@ def shadow_mats(source_cfg, qtypes, layer, seed=None):
     return mats
 
 
-def oracle_outputs(cfg, layer, x, logits, tokens, residual, seed=None, threads=8, mats=None):
+def oracle_outputs(cfg, layer, x, logits, tokens, residual, seed=None, threads=8, mats=None,
+                   qtypes_of=None):
     """Oracle output rows for `tokens` (bf16 [len(tokens)][d]).
 
     Routing comes from the oracle on `logits`; only the experts the tokens use
     are regenerated and evaluated.  Tokens are independent given their routing.
     `mats(e)`, if given, supplies expert e's three (codes, scales) in cfg's code
-    families instead of the synthetic generator.
+    families instead of the synthetic generator; `qtypes_of(e)`, if given, names the code
+    families of expert e's matrices in place of cfg's (per-expert mixed precision).
     """
     tokens = np.asarray(tokens)
     ids, w = oracle.topk_softmax(logits[tokens], cfg.k)
@@ -86,11 +88,12 @@ def oracle_outputs(cfg, layer, x, logits, tokens, residual, seed=None, threads=8
 
     def run(e):
         mm = mats(e) if mats else [synth.gen_matrix(cfg, layer, e, m, seed) for m in range(3)]
+        qt = qtypes_of(e) if qtypes_of else cfg.qtypes
         if e == cfg.E:
-            _, yy = oracle.expert_rows(cfg.qtypes, mm, xs)
+            _, yy = oracle.expert_rows(qt, mm, xs)
             return e, None, yy
         rows = by_expert[e]
-        _, yy = oracle.expert_rows(cfg.qtypes, mm, xs[[i for i, _ in rows]])
+        _, yy = oracle.expert_rows(qt, mm, xs[[i for i, _ in rows]])
         return e, rows, yy
 
     work = list(by_expert) + ([cfg.E] if cfg.n_shared else [])

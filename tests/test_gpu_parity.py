@@ -7,6 +7,8 @@ fp32 logits the GPU used, so that both sides take the integer decisions on
 the same values; the GPU's own logits are checked against the oracle's
 double-precision logits separately.
 """
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -53,7 +55,7 @@ def _run(dl, x_np, mode, flags=0, logits=None):
     return _host_u16(out), _routing_host(R, T, cfg.k)
 
 
-def _full_check(dl, x, mode, flags=0, logits=None, label="", mats=None):
+def _full_check(dl, x, mode, flags=0, logits=None, label="", mats=None, qtypes_of=None):
     cfg = dl.cfg
     print(f"[{label}] {mode} T={x.shape[0]} cfg={cfg.name}", flush=True)
     out, rt = _run(dl, x, mode, flags, logits)
@@ -67,7 +69,7 @@ def _full_check(dl, x, mode, flags=0, logits=None, label="", mats=None):
     check_routing_exact(cfg, used, rt)
     tokens = np.arange(x.shape[0])
     ref = oracle_outputs(cfg, dl.layer, x, used, tokens, bool(flags & bq.MOE_ADD_RESIDUAL),
-                         mats=mats)
+                         mats=mats, qtypes_of=qtypes_of)
     assert_parity(out, ref, f"{label} out")
     return out, rt
 
@@ -178,6 +180,43 @@ def test_shadow_of_3bit_experts(layers):
                 label="shadow", mats=mats)
     _full_check(dl, synth.gen_x(src), "prefill", logits=synth.gen_logits(src), label="shadow",
                 mats=mats)
+
+
+@pytest.mark.parametrize("alt_q", [(2, 2, 2), (1, 1, 1)])
+def test_per_expert_mixed_precision_decode(layers, alt_q):
+    # a second, lower-bit copy of the routed experts chosen per expert by a device mask:
+    # (2,2,2) keeps the down families equal (fused down + combine reads both copies),
+    # (1,1,1) does not (one filtered down launch per copy, then the combine)
+    src = synth.small_config(MULTI, name="shadow_src", q_gate=synth.QT_INT3,
+                             q_up=synth.QT_INT3, q_down=synth.QT_INT2, T=300)
+    main = layers("mix_main", src)
+    alt = layers(f"mix_alt{alt_q}", workloads.DeviceLayer(src, 0, DEV, shadow_qtypes=alt_q))
+    sel_np = (np.arange(src.E) % 3 == 1).astype(np.uint8)
+    ids1 = oracle.topk_softmax(synth.gen_logits(src, T=1), src.k)[0][0]
+    sel_np[ids1[0]], sel_np[ids1[1:]] = 1, 0  # the single token reads both copies
+    sel = torch.from_numpy(sel_np).to(DEV)
+    h = bq.make_layer(src.d, src.inter, src.E, src.k, src.n_shared, src.qtypes, main.experts,
+                      main.stride, main.shared, main.router_w, main.router_bias,
+                      alt=(alt.experts, alt.stride, alt_q, sel))
+    dl = types.SimpleNamespace(cfg=src, layer=0, handle=h)
+    shadow = shadow_mats(src, alt_q, 0)
+
+    def mats(e):
+        if e < src.E and sel_np[e]:
+            return shadow(e)
+        return [synth.gen_matrix(src, 0, e, m) for m in range(3)]
+
+    def qtypes_of(e):
+        return alt_q if e < src.E and sel_np[e] else src.qtypes
+
+    for T in (1, 8):
+        _, rt = _full_check(dl, synth.gen_x(src, T=T), "decode", logits=synth.gen_logits(src, T=T),
+                            label=f"mixed{alt_q}", mats=mats, qtypes_of=qtypes_of)
+        used = np.unique(rt["ids"][:T])
+        assert sel_np[used].any() and not sel_np[used].all()  # both copies were read
+    with pytest.raises(bq.MoeError) as ei:
+        _run(dl, synth.gen_x(src, T=8), "prefill", logits=synth.gen_logits(src, T=8))
+    assert ei.value.status == bq.MOE_ERR_UNSUPPORTED
 
 
 def test_prefill_int3_mixed(layers):

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(bq.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert bq.moe_abi_version() == 1
+    assert bq.moe_abi_version() == 2
 
 
 def test_ceilings_library_exports_every_declared_symbol():
@@ -138,7 +138,7 @@ def _layer(**kw):
     p.update(kw)
     return bq.make_layer(p["d"], p["inter"], p["n_experts"], p["top_k"], p["n_shared"],
                          p["qtypes"], p["experts"], p["expert_stride"], p["shared"],
-                         p["router_w"], p["router_bias"])
+                         p["router_w"], p["router_bias"], p.get("alt"))
 
 
 def _routing():
@@ -184,6 +184,25 @@ def test_argument_errors_return_status(fn):
         assert _call(fn, L, 2, out=FAKE + 256) == bq.MOE_ERR_INVALID_ARG  # overlaps x
         assert _call(fn, L, 2, out=None) == bq.MOE_ERR_INVALID_ARG
         assert _call(fn, L, 2, x=FAKE + 2) == bq.MOE_ERR_INVALID_ARG
+
+
+ALT = (FAKE + (1 << 34), 30_720, (1, 1, 1), FAKE + (1 << 35))  # a valid second copy
+
+
+@pytest.mark.parametrize("fn", ["moe_forward_decode", "moe_forward_prefill"])
+def test_second_expert_copy_checks(fn):
+    ae, st, q, sel = ALT
+    assert _call(fn, _layer(alt=(ae, st, (1, 4, 1), sel)), 2) == bq.MOE_ERR_UNSUPPORTED
+    assert _call(fn, _layer(alt=(ae, st, q, None)), 2) == bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, _layer(alt=(ae, 512, q, sel)), 2) == bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, _layer(alt=(ae, st + 8, q, sel)), 2) == bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, _layer(alt=(ae + 64, st, q, sel)), 2) == bq.MOE_ERR_INVALID_ARG
+    # valid second copy: prefill refuses it, decode goes on to its other checks
+    want = bq.MOE_ERR_UNSUPPORTED if fn == "moe_forward_prefill" else bq.MOE_ERR_INVALID_ARG
+    assert _call(fn, _layer(alt=ALT), 2, out=None) == want
+    # the router alone never reads expert weights
+    assert _call("moe_route_topk", _layer(alt=(ae, st, q, None)), 2, ws_bytes=10) == \
+        bq.MOE_ERR_WORKSPACE
 
 
 def test_decode_token_range():
