@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 // Decode router logits (TT = T <= 8 tokens, a compile-time count so that
 // every load of a step is unconditional and all of them are in flight
 // together): block per expert, its 4 waves split d; the router row is read
-// once for all T tokens and the partial sums meet in LDS.  The blocks also
-// stage x for the expert kernels: xs = x/16 (exact) and, per 32-group, the
+// once for all T tokens and the partial sums meet in LDS.  The blocks after
+// the E logit blocks stage x for the expert kernels: xs = x/16 (exact) and, per 32-group, the
 // staged sums of the correction term (see stage_sums in device_common.h).
 template <int TT>
 __global__ __launch_bounds__(256) void k_dec_logits(const uint16_t* __restrict__ x, int T, int d,
@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void k_dec_logits(const uint16_t* __restrict__
   __shared__ float s_part[4][TT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int e = blockIdx.x;
-  if (do_logits && e < E) {
+  const int nlog = do_logits ? E : 0;  // blocks [0, nlog): one logit each; the rest stage x
+  if (e < nlog) {
     float acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = 0.f;
@@ -102,11 +103,13 @@ __global__ __launch_bounds__(256) void k_dec_logits(const uint16_t* __restrict__
       logits[(size_t)tid * E + e] = s + (bias ? bias[e] : 0.f);
     }
   }
-  // staging: one 32-lane half-wave per (token, group), spread over the grid
+  // staging: one 32-lane half-wave per (token, group), on blocks of their own so
+  // that it runs beside the logits instead of after them
+  if (e < nlog) return;
   const int G = d / 32;
   const int pairs = T * G;
   const int half = tid >> 5, j = tid & 31;
-  for (int p = blockIdx.x * 8 + half; p < pairs; p += gridDim.x * 8) {
+  for (int p = (e - nlog) * 8 + half; p < pairs; p += (gridDim.x - nlog) * 8) {
     const int t = p / G, g = p % G;
     const uint32_t xb = x[(size_t)t * d + g * 32 + j];
     const float xf = bf16_to_f32(xb);
@@ -476,7 +479,7 @@ int launch_decode_route(const moe_layer* L, const uint16_t* x, int T, uint32_t f
   const int do_logits = !(flags & MOE_LOGITS_GIVEN);
   if (mask & MOE_DECODE_STAGE_ROUTE) {
     const int G = d / 32;
-    dim3 grid(max(E, (T * G + 7) / 8));
+    dim3 grid((do_logits ? E : 0) + (T * G + 7) / 8);
 #define BQ_LG(TT)                                                                             \
   case TT:                                                                                    \
     hipLaunchKernelGGL(k_dec_logits<TT>, grid, dim3(256), 0, s, x, T, d, E, L->router_w,      \
