@@ -209,11 +209,23 @@ def test_per_expert_mixed_precision_decode(layers, alt_q):
     def qtypes_of(e):
         return alt_q if e < src.E and sel_np[e] else src.qtypes
 
-    for T in (1, 8):
-        _, rt = _full_check(dl, synth.gen_x(src, T=T), "decode", logits=synth.gen_logits(src, T=T),
-                            label=f"mixed{alt_q}", mats=mats, qtypes_of=qtypes_of)
+    for T in (1, 4, 8):
+        x_np, lg_np = synth.gen_x(src, T=T), synth.gen_logits(src, T=T)
+        full, rt = _full_check(dl, x_np, "decode", logits=lg_np, label=f"mixed{alt_q}",
+                               mats=mats, qtypes_of=qtypes_of)
         used = np.unique(rt["ids"][:T])
         assert sel_np[used].any() and not sel_np[used].all()  # both copies were read
+        # the stages one call at a time give the full call's output bit for bit
+        x = _to_dev_u16(x_np)
+        R = bq.alloc_routing(T, src.E, src.k, DEV,
+                             logits=torch.from_numpy(np.ascontiguousarray(lg_np)).to(DEV))
+        ws = bq.alloc_workspace(h, T, DEV)
+        out = torch.zeros((T, src.d), dtype=torch.int16, device=DEV)
+        for st in (bq.MOE_DECODE_STAGE_ROUTE, bq.MOE_DECODE_STAGE_SELECT,
+                   bq.MOE_DECODE_STAGE_GATEUP, bq.MOE_DECODE_STAGE_DOWN):
+            bq.moe_forward_decode_stages(h, x, T, bq.MOE_LOGITS_GIVEN, R, ws, out, st)
+        torch.cuda.synchronize()
+        assert np.array_equal(_host_u16(out), full), T
     with pytest.raises(bq.MoeError) as ei:
         _run(dl, synth.gen_x(src, T=8), "prefill", logits=synth.gen_logits(src, T=8))
     assert ei.value.status == bq.MOE_ERR_UNSUPPORTED
