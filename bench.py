@@ -86,7 +86,9 @@ def parse():
     ap.add_argument("--extra", default="c2,c2s,c4",
                     help="further workloads measured after the headline ones and reported in "
                          "the same line: c2 (decode, 8 tokens), c2s (c2 through a 2-bit shadow "
-                         "of its 3-bit experts), c4 (4-layer prefill stack); 'none' skips them")
+                         "of its 3-bit experts), c4 (4-layer prefill stack), c2m (c2 with its 64 "
+                         "most favoured experts read from a 2-bit copy; not run by default); "
+                         "'none' skips them")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured roofline ceilings (read stream, matrix-core peak)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -115,25 +117,55 @@ def decode_leg(args, dev):
     shared = [base.shared] + [None if base.shared is None else base.shared.clone()
                               for _ in range(C - 1)]
     handles = [base.make_handle(e, s) for e, s in zip(experts, shared)]
+    # per-expert mixed precision: a second copy of the routed experts in the families
+    # alt_q, read for the n_alt experts the router bias favours most
+    alt = getattr(args, "alt", None)
+    sel_np = np.zeros(cfg.E, bool)
+    fam = {False: cfg.qtypes}
+    if alt is not None:
+        alt_q, n_alt = alt
+        adl = workloads.DeviceLayer(cfg, 0, dev, shadow_qtypes=alt_q)
+        bias = synth.gen_bias(cfg, 0) if cfg.router else None
+        order = np.argsort(-bias, kind="stable") if bias is not None else np.arange(cfg.E)
+        sel_np[order[:n_alt]] = True
+        sel = torch.from_numpy(sel_np.astype(np.uint8)).to(dev)
+        alt_ex = [adl.experts] + [adl.experts.clone() for _ in range(C - 1)]
+        handles = [bq.make_layer(cfg.d, cfg.inter, cfg.E, cfg.k, cfg.n_shared, cfg.qtypes, e,
+                                 base.stride, s_, base.router_w, base.router_bias,
+                                 alt=(a_, adl.stride, alt_q, sel))
+                   for e, s_, a_ in zip(experts, shared, alt_ex)]
+        fam[True] = tuple(alt_q)
+
+    def copy_bytes(counts, gateup_only=False):
+        # packed bytes one step reads: each active routed expert from its copy, plus shared
+        act = counts.cpu().numpy() > 0
+        def per(q):
+            if gateup_only:
+                return (bq.moe_packed_bytes(q[0], cfg.d, cfg.inter) +
+                        bq.moe_packed_bytes(q[1], cfg.d, cfg.inter))
+            return bq.moe_expert_bytes(*q, cfg.d, cfg.inter)
+        n_alt_act = int((act & sel_np).sum())
+        return ((int(act.sum()) - n_alt_act + cfg.n_shared) * per(fam[False]) +
+                n_alt_act * (per(fam[True]) if n_alt_act else 0))
     n = W + K
     X = synth.gen_x(cfg, T=T * n).reshape(n, T, cfg.d)
     xd = torch.from_numpy(X.view(np.int16)).to(dev)
     R = bq.alloc_routing(T, cfg.E, cfg.k, dev)
     ws = bq.alloc_workspace(handles[0], T, dev)
     out = torch.empty((T, cfg.d), dtype=torch.int16, device=dev)
-    ebytes = bq.moe_expert_bytes(*cfg.qtypes, cfg.d, cfg.inter)
     router_bytes = cfg.E * cfg.d * 4 if cfg.router else 0
 
     def step(i):
         bq.moe_forward_decode(handles[i % C], xd[i], T, 0, R, ws, out)
 
     # bytes streamed per step: each active expert (and the shared one) once
-    active = []
+    active, step_bytes = [], []
     for i in range(W, n):
         step(i)
         active.append(int((R.counts > 0).sum().item()) + cfg.n_shared)
+        step_bytes.append(copy_bytes(R.counts))
     torch.cuda.synchronize()
-    bytes_per_step = float(np.mean(active)) * ebytes
+    bytes_per_step = float(np.mean(step_bytes))
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
@@ -167,9 +199,7 @@ def decode_leg(args, dev):
     gu_bytes = []
     for j in range(C):
         bq.moe_forward_decode(handles[j], xd[j], T, 0, Rs[j], wss[j], outs[j])
-        gu_bytes.append((int((Rs[j].counts > 0).sum().item()) + cfg.n_shared) *
-                        (bq.moe_packed_bytes(cfg.q_gate, cfg.d, cfg.inter) +
-                         bq.moe_packed_bytes(cfg.q_up, cfg.d, cfg.inter)))
+        gu_bytes.append(copy_bytes(Rs[j].counts, gateup_only=True))
     torch.cuda.synchronize()
     GU = bq.MOE_DECODE_STAGE_GATEUP
     if args.kernel_loop:
@@ -200,8 +230,7 @@ def decode_leg(args, dev):
     # the down projection (+ combine) re-runs on each copy's h from the gate/up runs above
     dn_us = stage_us(bq.MOE_DECODE_STAGE_DOWN)
     gu_b = float(np.mean([gu_bytes[r % C] for r in range(reps)]))
-    exp_b = float(np.mean([
-        (int((Rs[r % C].counts > 0).sum().item()) + cfg.n_shared) * ebytes for r in range(C)]))
+    exp_b = float(np.mean([copy_bytes(Rs[r % C].counts) for r in range(C)]))
 
     # warm: the same layer copy and token every step (its experts stay in the
     # last-level cache), K steps as one graph
@@ -540,6 +569,20 @@ def extra_legs(args, dev):
         gbs = d["bytes_per_step"] / (d["ms"] * 1e-3) / 1e9
         out["decode_c2_shadow"] = {
             "workload": "c2_decode_t8_zipf, gate/up read from a 2-bit shadow of the 3-bit experts",
+            "T": d["cfg"].T, "steps": a.steps, "layer_copies": a.copies,
+            "us_per_layer": d["ms"] * 1e3, "packed_expert_bytes_per_step": d["bytes_per_step"],
+            "unique_routed_experts_per_step": d["active"] - d["cfg"].n_shared,
+            "gbs": gbs, "decode_kernels": d["kernels"]}
+    if "c2m" in want:
+        # C2 with per-expert mixed precision: the 64 experts the router bias favours most
+        # read from a 2-bit copy, the rest from the 3-bit experts (one layer handle)
+        a = argparse.Namespace(**vars(args))
+        a.config, a.steps, a.warmup, a.copies, a.kernel_loop = "c2", 50, 5, 4, 0
+        a.alt = ((2, 2, 2), 64)
+        d = decode_leg(a, dev)
+        gbs = d["bytes_per_step"] / (d["ms"] * 1e-3) / 1e9
+        out["decode_c2_mixed"] = {
+            "workload": "c2_decode_t8_zipf, the 64 most favoured experts read from a 2-bit copy",
             "T": d["cfg"].T, "steps": a.steps, "layer_copies": a.copies,
             "us_per_layer": d["ms"] * 1e3, "packed_expert_bytes_per_step": d["bytes_per_step"],
             "unique_routed_experts_per_step": d["active"] - d["cfg"].n_shared,

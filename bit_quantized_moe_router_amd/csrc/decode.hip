@@ -585,7 +585,7 @@ __device__ __forceinline__ void dec_select_one_token(const DecRoute& ro, int slo
 // offsets, permutation, slot list), for the down projection and the caller.
 template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KSPLIT, int KBW, bool ONE_ROW,
           bool ROUTE = false>
-__global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
+__device__ __forceinline__ void dec_proj_body(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ slots, const uint16_t* __restrict__ A,
     const uint8_t* __restrict__ Asum, int K, int N, int Mmax, float ca, float cb,
@@ -731,6 +731,42 @@ __global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
       out[(size_t)(row0 + row) * N + (nt[0] + j) * 16 + col] = (uint16_t)f32_to_bf16(s);
     }
   }
+}
+
+template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, int KSPLIT, int KBW, bool ONE_ROW,
+          bool ROUTE = false>
+__global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj(
+    const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
+    ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ slots, const uint16_t* __restrict__ A,
+    const uint8_t* __restrict__ Asum, int K, int N, int Mmax, float ca, float cb,
+    uint16_t* __restrict__ out, float* __restrict__ out_psum, Unpack2K uk, DecRoute ro,
+    int want_alt) {
+  dec_proj_body<GATEUP, QA3, QB3, SAMEC, KSPLIT, KBW, ONE_ROW, ROUTE>(
+      experts, stride, shared, pa, pb, slots, A, Asum, K, N, Mmax, ca, cb, out, out_psum, uk, ro,
+      want_alt);
+}
+
+// Both expert copies in one launch: each block reads its slot's copy flag
+// (uniform over the block) and runs the projection on that copy's blobs,
+// code families (QA3.. for the first copy, XA3.. for the second) and offsets.
+template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, bool XA3, bool XB3, bool XSAMEC,
+          int KSPLIT, int KBW, bool ONE_ROW>
+__global__ __launch_bounds__(64 * KSPLIT) void k_dec_proj_mixed(
+    const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
+    ProjDesc pa, ProjDesc pb, const uint8_t* __restrict__ alt_experts, size_t alt_stride,
+    ProjDesc xpa, ProjDesc xpb, const int32_t* __restrict__ slots, const uint16_t* __restrict__ A,
+    const uint8_t* __restrict__ Asum, int K, int N, int Mmax, float ca, float cb, float xca,
+    float xcb, uint16_t* __restrict__ out, float* __restrict__ out_psum, Unpack2K uk) {
+  const int groups = N / (16 * (GATEUP ? 1 : 4));
+  const int slot = blockIdx.x / groups;
+  if (slots[kSlotRec * (1 + slot) + 3] != 0)
+    dec_proj_body<GATEUP, XA3, XB3, XSAMEC, KSPLIT, KBW, ONE_ROW>(
+        alt_experts, alt_stride, shared, xpa, xpb, slots, A, Asum, K, N, Mmax, xca, xcb, out,
+        out_psum, uk, DecRoute{}, 1);
+  else
+    dec_proj_body<GATEUP, QA3, QB3, SAMEC, KSPLIT, KBW, ONE_ROW>(
+        experts, stride, shared, pa, pb, slots, A, Asum, K, N, Mmax, ca, cb, out, out_psum, uk,
+        DecRoute{}, 0);
 }
 
 // ------------------------------------------------- down projection + combine
@@ -982,6 +1018,59 @@ static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const
   return 0;
 }
 
+// Both copies in one launch (k_dec_proj_mixed); same launch shapes as launch_proj.
+template <bool GATEUP, bool QA3, bool QB3, bool SAMEC, bool XA3, bool XB3, bool XSAMEC>
+static int launch_proj_mixed(DecShape sh, int n_blocks, int Mmax, hipStream_t s,
+                             const moe_layer* L, ProjDesc pa, ProjDesc pb, ProjDesc xpa,
+                             ProjDesc xpb, const int32_t* slots, const uint16_t* A,
+                             const uint8_t* Asum, int K, int N, float ca, float cb, float xca,
+                             float xcb, uint16_t* out, float* psum) {
+  const size_t lds = dec_lds_bytes(GATEUP, sh, Mmax);
+  const uint8_t* ex = (const uint8_t*)L->experts;
+  const uint8_t* ax = (const uint8_t*)L->alt_experts;
+  const uint8_t* shb = (const uint8_t*)L->shared;
+#define BQ_M(KS, KBW)                                                                          \
+  do {                                                                                         \
+    if (Mmax == 1)                                                                             \
+      hipLaunchKernelGGL(                                                                      \
+          (k_dec_proj_mixed<GATEUP, QA3, QB3, SAMEC, XA3, XB3, XSAMEC, KS, KBW, true>),        \
+          dim3(n_blocks), dim3(64 * KS), lds, s, ex, L->expert_stride, shb, pa, pb, ax,        \
+          L->alt_stride, xpa, xpb, slots, A, Asum, K, N, Mmax, ca, cb, xca, xcb, out, psum,    \
+          kUnpack2);                                                                           \
+    else if constexpr (KS < 16)                                                                \
+      hipLaunchKernelGGL(                                                                      \
+          (k_dec_proj_mixed<GATEUP, QA3, QB3, SAMEC, XA3, XB3, XSAMEC, KS, KBW, false>),       \
+          dim3(n_blocks), dim3(64 * KS), lds, s, ex, L->expert_stride, shb, pa, pb, ax,        \
+          L->alt_stride, xpa, xpb, slots, A, Asum, K, N, Mmax, ca, cb, xca, xcb, out, psum,    \
+          kUnpack2);                                                                           \
+    else                                                                                       \
+      return -1;                                                                               \
+  } while (0)
+  if (sh.ksplit == 4 && sh.kbw == 2)
+    BQ_M(4, 2);
+  else if (sh.ksplit == 4 && sh.kbw == 4)
+    BQ_M(4, 4);
+  else if constexpr (GATEUP) {
+    if (sh.ksplit == 4 && sh.kbw == 8)
+      BQ_M(4, 8);
+    else if (sh.ksplit == 8 && sh.kbw == 8)
+      BQ_M(8, 8);
+    else
+      return -1;
+  } else {
+    if (sh.ksplit == 8 && sh.kbw == 4)
+      BQ_M(8, 4);
+    else if (sh.ksplit == 16 && sh.kbw == 4)
+      BQ_M(16, 4);
+    else if (sh.ksplit == 8 && sh.kbw == 8)
+      BQ_M(8, 8);
+    else
+      return -1;
+  }
+#undef BQ_M
+  return 0;
+}
+
 // Single-token gate/up makes the expert selection itself (see
 // dec_select_one_token) for up to 256 experts; a call that runs the gate/up
 // stage then skips the select kernel.
@@ -1047,11 +1136,32 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
                             R->topk_ids, R->topk_w,    R->counts, R->offsets,  R->perm_tok,
                             R->inv_row,  (int32_t*)(ws + W.slots)};
     const DecRoute* rp = fused_select ? &route : nullptr;
-    rc = launch_gateup(L, sh, nb, Mmax, s, slots, xs, xsum, hs, hsum, rp, has_alt ? 0 : -1);
-    if (rc) return rc;
-    if (has_alt) {
-      rc = launch_gateup(&La, sh, nb, Mmax, s, slots, xs, xsum, hs, hsum, nullptr, 1);
+    if (has_alt && L->q_gate == L->q_up && La.q_gate == La.q_up) {
+      // both copies in one launch (gate and up share a family within each copy)
+      const bool m3 = L->q_gate == MOE_Q_INT3, a3 = La.q_gate == MOE_Q_INT3;
+      const ProjDesc pg = proj(L, 0), pu = proj(L, 1), xg = proj(&La, 0), xu = proj(&La, 1);
+      const float cm = qtype_offset(L->q_gate), ca = qtype_offset(La.q_gate);
+#define BQ_GM(M3, A3)                                                                          \
+  rc = launch_proj_mixed<true, M3, M3, true, A3, A3, true>(sh, nb, Mmax, s, L, pg, pu, xg, xu, \
+                                                           slots, xs, xsum, d, I, cm, cm, ca,  \
+                                                           ca, hs, hsum)
+      if (m3 && a3)
+        BQ_GM(true, true);
+      else if (m3)
+        BQ_GM(true, false);
+      else if (a3)
+        BQ_GM(false, true);
+      else
+        BQ_GM(false, false);
+#undef BQ_GM
       if (rc) return rc;
+    } else {
+      rc = launch_gateup(L, sh, nb, Mmax, s, slots, xs, xsum, hs, hsum, rp, has_alt ? 0 : -1);
+      if (rc) return rc;
+      if (has_alt) {
+        rc = launch_gateup(&La, sh, nb, Mmax, s, slots, xs, xsum, hs, hsum, nullptr, 1);
+        if (rc) return rc;
+      }
     }
   }
   // the fused down + combine takes both copies when their down families agree
@@ -1100,17 +1210,34 @@ int launch_decode(const moe_layer* L, const uint16_t* x, int T, uint32_t flags, 
     const DecShape sh = dec_shape(false, I, Mmax);
     const int nb = W.max_slots * (d / 64);
     const uint8_t* hsb = (const uint8_t*)hsum;
-    for (int copy = 0; copy < (has_alt ? 2 : 1); ++copy) {
-      const moe_layer* Lc = copy ? &La : L;
-      const ProjDesc pd = proj(Lc, 2);
-      const float cd = qtype_offset(Lc->q_down);
-      const int want = has_alt ? copy : -1;
-      if (Lc->q_down == MOE_Q_INT3)
-        rc = launch_proj<false, true, true, true>(sh, nb, Mmax, s, Lc, pd, pd, slots, hs, hsb, I,
-                                                  d, cd, cd, y, nullptr, nullptr, want);
+    if (has_alt) {
+      // both copies in one launch
+      const bool m3 = L->q_down == MOE_Q_INT3, a3 = La.q_down == MOE_Q_INT3;
+      const ProjDesc pd = proj(L, 2), xpd = proj(&La, 2);
+      const float cd = qtype_offset(L->q_down), xcd = qtype_offset(La.q_down);
+#define BQ_DM(M3, A3)                                                                          \
+  rc = launch_proj_mixed<false, M3, M3, true, A3, A3, true>(sh, nb, Mmax, s, L, pd, pd, xpd,   \
+                                                            xpd, slots, hs, hsb, I, d, cd, cd, \
+                                                            xcd, xcd, y, nullptr)
+      if (m3 && a3)
+        BQ_DM(true, true);
+      else if (m3)
+        BQ_DM(true, false);
+      else if (a3)
+        BQ_DM(false, true);
       else
-        rc = launch_proj<false, false, false, true>(sh, nb, Mmax, s, Lc, pd, pd, slots, hs, hsb,
-                                                    I, d, cd, cd, y, nullptr, nullptr, want);
+        BQ_DM(false, false);
+#undef BQ_DM
+      if (rc) return rc;
+    } else {
+      const ProjDesc pd = proj(L, 2);
+      const float cd = qtype_offset(L->q_down);
+      if (L->q_down == MOE_Q_INT3)
+        rc = launch_proj<false, true, true, true>(sh, nb, Mmax, s, L, pd, pd, slots, hs, hsb, I,
+                                                  d, cd, cd, y, nullptr, nullptr, -1);
+      else
+        rc = launch_proj<false, false, false, true>(sh, nb, Mmax, s, L, pd, pd, slots, hs, hsb,
+                                                    I, d, cd, cd, y, nullptr, nullptr, -1);
       if (rc) return rc;
     }
     rc = launch_combine(y, T, d, k, L->n_shared, R->inv_row, R->topk_w, x,
