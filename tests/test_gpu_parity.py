@@ -182,11 +182,13 @@ def test_shadow_of_3bit_experts(layers):
                 mats=mats)
 
 
-@pytest.mark.parametrize("alt_q", [(2, 2, 2), (1, 1, 1)])
+@pytest.mark.parametrize("alt_q", [(2, 2, 2), (1, 1, 1), (2, 1, 1)])
 def test_per_expert_mixed_precision_decode(layers, alt_q):
-    # a second, lower-bit copy of the routed experts chosen per expert by a device mask:
-    # (2,2,2) keeps the down families equal (fused down + combine reads both copies),
-    # (1,1,1) does not (one filtered down launch per copy, then the combine)
+    # a second, lower-bit copy of the routed experts chosen per expert by a device mask.
+    # Gate/up: one launch over both copies when gate and up share a family within each
+    # copy, else one filtered launch per copy ((2,1,1)).  Down: the fused down + combine
+    # reads both copies when the down families agree ((2,2,2) at a single token), else one
+    # launch over both copies, then the combine
     src = synth.small_config(MULTI, name="shadow_src", q_gate=synth.QT_INT3,
                              q_up=synth.QT_INT3, q_down=synth.QT_INT2, T=300)
     main = layers("mix_main", src)
