@@ -457,7 +457,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the whole layer (all experts) fits in one MI355X's HBM "
-              "and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+              "and the library has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 
