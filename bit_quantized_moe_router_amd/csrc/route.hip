@@ -56,6 +56,32 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   }
 }
 
+// Sum over the 64 lanes by DPP lane moves and the gfx950 lane swaps (no LDS
+// round trips): each step adds a lane's value to that of a partner lane in a
+// disjoint pairing (xor 1, xor 2, the mirror within 8 lanes, within 16 lanes,
+// then rows 2m/2m+1 and the two halves), so every lane ends with the same sum.
+__device__ __forceinline__ float dpp_f32(float v, int which) {
+  const int b = __float_as_int(v);
+  switch (which) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));   // [2,3,0,1]
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, true));  // half mirror
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x140, 0xF, 0xF, true)); // mirror
+  }
+}
+__device__ __forceinline__ float wave_sum_lanes(float v) {
+  v += dpp_f32(v, 0);
+  v += dpp_f32(v, 1);
+  v += dpp_f32(v, 2);
+  v += dpp_f32(v, 3);
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Decode router logits (TT = T <= 8 tokens, a compile-time count so that
 // every load of a step is unconditional and all of them are in flight
 // together): block per expert, its 4 waves split d; the router row is read
@@ -78,23 +104,29 @@ __global__ __launch_bounds__(256) void k_dec_logits(const uint16_t* __restrict__
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = 0.f;
     const float* w = Wr + (size_t)e * d;
-#pragma unroll 4
-    for (int i = tid * 4; i < d; i += 1024) {
-      const float4 wv = *reinterpret_cast<const float4*>(w + i);
-      uint2 xv[TT];
+    // 8 consecutive entries per lane and step (d is a multiple of 128)
+#pragma unroll 2
+    for (int i = tid * 8; i < d; i += 2048) {
+      const float4 w0 = *reinterpret_cast<const float4*>(w + i);
+      const float4 w1 = *reinterpret_cast<const float4*>(w + i + 4);
+      uint4 xv[TT];
 #pragma unroll
-      for (int t = 0; t < TT; ++t) xv[t] = *reinterpret_cast<const uint2*>(x + (size_t)t * d + i);
+      for (int t = 0; t < TT; ++t) xv[t] = *reinterpret_cast<const uint4*>(x + (size_t)t * d + i);
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        acc[t] = fmaf(bf16_to_f32(xv[t].x & 0xFFFFu), wv.x, acc[t]);
-        acc[t] = fmaf(bf16_to_f32(xv[t].x >> 16), wv.y, acc[t]);
-        acc[t] = fmaf(bf16_to_f32(xv[t].y & 0xFFFFu), wv.z, acc[t]);
-        acc[t] = fmaf(bf16_to_f32(xv[t].y >> 16), wv.w, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].x & 0xFFFFu), w0.x, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].x >> 16), w0.y, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].y & 0xFFFFu), w0.z, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].y >> 16), w0.w, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].z & 0xFFFFu), w1.x, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].z >> 16), w1.y, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].w & 0xFFFFu), w1.z, acc[t]);
+        acc[t] = fmaf(bf16_to_f32(xv[t].w >> 16), w1.w, acc[t]);
       }
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      const float s = wave_sum(acc[t]);
+      const float s = wave_sum_lanes(acc[t]);
       if (lane == 0) s_part[wave][t] = s;
     }
     __syncthreads();
