@@ -312,6 +312,21 @@ __device__ __forceinline__ void dec_mfma_kb_band(int i, f32x4 (&acc)[NS],
   }
 }
 
+// Sum over a 16-lane row, left in all of its lanes: each step adds the value
+// of a partner lane in a disjoint pairing (xor 1, xor 2, the mirror within 8
+// lanes, the mirror within 16 lanes).
+__device__ __forceinline__ float row16_sum(float v) {
+  int b = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  b = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+  b = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, true));  // half mirror
+  b = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x140, 0xF, 0xF, true));  // mirror
+  return v;
+}
+
 // The four lane quarters (groups) of a column added: lanes 0..15 then hold
 // rows 0..MR-1 in elements 0..MR-1, the matrix-core layout of rows 0..3.
 template <int NS, int MR>
@@ -322,8 +337,14 @@ __device__ __forceinline__ void dec_band_fold(f32x4 (&acc)[NS]) {
     for (int m = 0; m < 4; ++m) {
       float v = m < MR ? acc[j][m] : 0.f;
       if (m < MR) {
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
+        // partner lanes l ^ 16, then l ^ 32, by the gfx950 lane swaps (each
+        // lane adds the same two values in the same order)
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+        v = __uint_as_float(q[0]) + __uint_as_float(q[1]);
       }
       acc[j][m] = v;
     }
@@ -712,12 +733,11 @@ __device__ __forceinline__ void dec_proj_body(
       }
       // (W, S) of h over this tile's 16 columns: k-slots 16*(grp%2) + col of
       // the down projection's 32-group grp/2
+      // (sums over the 16 lanes of the row by DPP moves: xor 1, xor 2, then
+      // the mirrors within 8 and 16 lanes)
       float sw = hf * slot_weight(16 * (grp & 1) + col), s = hf;
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        sw += __shfl_xor(sw, o, 16);
-        s += __shfl_xor(s, o, 16);
-      }
+      sw = row16_sum(sw);
+      s = row16_sum(s);
       if (row < M && col == 0)
         *reinterpret_cast<float2*>(out_psum + ((size_t)(row0 + row) * (N / 16) + grp) * 2) =
             make_float2(sw, s);
