@@ -16,6 +16,7 @@ import torch  # load torch's HIP runtime first: libbqmoe.so binds to the same on
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbqmoe.so")
+ABI_VERSION = 2  # moe_abi_version() of the include/moe.h this binding follows
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_BAD_CODES, \
     MOE_ERR_DEVICE = range(6)
@@ -98,6 +99,10 @@ def load():
         f.restype = i32
     lib.moe_status_string.argtypes, lib.moe_status_string.restype = [i32], ctypes.c_char_p
     lib.moe_abi_version.argtypes, lib.moe_abi_version.restype = [], i32
+    if lib.moe_abi_version() != ABI_VERSION:
+        # moe_layer's layout depends on it: a stale build would misread every layer
+        raise ImportError(f"{LIB_PATH}: ABI version {lib.moe_abi_version()}, this binding needs "
+                          f"{ABI_VERSION}; rebuild the library")
     _lib = lib
     return lib
 
