@@ -17,7 +17,8 @@ import bit_quantized_moe_router_amd as bq
 import oracle
 import synth
 import workloads
-from helpers import assert_parity, check_routing_exact, oracle_outputs, shadow_mats
+from helpers import (assert_parity, check_routing_exact, oracle_outputs, shadow_mats,
+                     stratified_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -338,50 +339,141 @@ def test_prefill_stages_one_by_one_and_rerun(layers, q):
         assert np.array_equal(_host_u16(out), full), st
 
 
-def test_c3_prefill_full_sampled(layers):
+# Row-tile heights of the grouped GEMMs: 64-row tiles for 2-bit / 3-bit layers, 128-row tiles
+# for all-ternary layers.  The stratified samples reach every tile of these heights.
+TILE_ROWS_INT = 64
+TILE_ROWS_TERNARY = 128
+
+
+def _assert_cover(cov, n_shared):
+    print(f"  sample coverage: {cov}", flush=True)
+    assert cov["tokens"] >= 256
+    assert cov["tiles_reached"] == cov["tiles"]
+    assert cov["active_reached"] == cov["active"]
+    if n_shared:
+        assert cov["shared_reached"] == cov["shared_blocks"]
+
+
+@pytest.mark.timeout(600)
+def test_c3_prefill_stratified(layers):
+    """C3 at full size: routing bit-exact over all 8192 tokens, and the output of a
+    stratified sample of >= 256 tokens whose rows reach every 64-row tile of every active
+    expert (and every 64-token block of the shared expert) against the oracle."""
     dl = layers("c3")
     cfg = dl.cfg
     x = synth.gen_x(cfg)
     logits = synth.gen_logits(cfg)
     print("[c3] prefill T=8192", flush=True)
     out, rt = _run(dl, x, "prefill", logits=logits)
-    ids, *_ = check_routing_exact(cfg, logits, rt)
-    counts = rt["counts"]
-    hot = int(np.argmax(counts))
-    cold = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
-    toks = {0, cfg.T - 1, 1, cfg.T // 2}
-    toks |= set(np.where((ids == hot).any(1))[0][:3].tolist())
-    toks |= set(np.where((ids == cold).any(1))[0][:3].tolist())
-    toks = np.array(sorted(toks))
+    check_routing_exact(cfg, logits, rt)
+    toks, cov = stratified_tokens(rt["counts"], rt["offsets"], rt["perm_tok"], rt["inv_row"],
+                                  cfg.T, TILE_ROWS_INT, cfg.n_shared, seed=3)
+    _assert_cover(cov, cfg.n_shared)
     ref = oracle_outputs(cfg, 0, x, logits, toks, False)
-    assert_parity(out[toks], ref, "c3 sampled out")
+    assert_parity(out[toks], ref, "c3 stratified out")
 
 
-def test_c4_stack_full_sampled(layers):
+@pytest.mark.timeout(900)
+def test_c4_stack_stratified_and_end_to_end(layers):
+    """C4, four ternary layers with the residual, at full size.
+
+    Per layer: routing bit-exact over all 16384 tokens, and a stratified sample reaching
+    every 128-row tile of every active expert checked against the oracle fed this layer's
+    GPU input.  End to end: 128 tokens (the first, the last and random ones) carried through
+    all four layers by the oracle on its own outputs, compared with the GPU's last layer."""
     cfg = synth.CONFIGS["c4"]
     x = synth.gen_x(cfg)
+    rng = np.random.default_rng(4)
+    e2e_toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 126, replace=False)]))
+    x_e2e = x[e2e_toks].copy()
     for layer in range(cfg.layers):
         print(f"[c4] building layer {layer}", flush=True)
         dl = workloads.DeviceLayer(cfg, layer, DEV)
         logits = synth.gen_logits(cfg, layer)
         out, rt = _run(dl, x, "prefill", flags=bq.MOE_ADD_RESIDUAL, logits=logits)
-        ids, *_ = check_routing_exact(cfg, logits, rt)
+        check_routing_exact(cfg, logits, rt)
         counts = rt["counts"]
         print(f"  layer {layer}: max rows/expert {counts.max()}, empty experts "
               f"{int((counts == 0).sum())}", flush=True)
-        hot = int(np.argmax(counts))
-        toks = {0, cfg.T - 1, 7}
-        toks |= set(np.where((ids == hot).any(1))[0][-2:].tolist())
-        nz = np.where(counts > 0)[0]
-        rare = int(nz[np.argmin(counts[nz])])
-        toks |= set(np.where((ids == rare).any(1))[0][:2].tolist())
-        toks = np.array(sorted(toks))
-        # per-layer check: the oracle gets this layer's GPU input
-        ref = oracle_outputs(cfg, layer, x, logits, toks, True)
-        assert_parity(out[toks], ref, f"c4 layer {layer} sampled out")
+        toks, cov = stratified_tokens(counts, rt["offsets"], rt["perm_tok"], rt["inv_row"],
+                                      cfg.T, TILE_ROWS_TERNARY, cfg.n_shared, seed=40 + layer)
+        _assert_cover(cov, cfg.n_shared)
+        # one pass of the oracle over this layer's experts serves both checks
+        x_cat = np.concatenate([x[toks], x_e2e])
+        lg_cat = np.concatenate([logits[toks], logits[e2e_toks]])
+        ref = oracle_outputs(cfg, layer, x_cat, lg_cat, np.arange(len(x_cat)), True)
+        assert_parity(out[toks], ref[: len(toks)], f"c4 layer {layer} per-layer")
+        x_e2e = ref[len(toks):]
+        st = assert_parity(out[e2e_toks], x_e2e, f"c4 after layer {layer} end-to-end")
         x = out  # next layer's input
         del dl
         torch.cuda.empty_cache()
+    print(f"  c4 end-to-end over {cfg.layers} layers: {st}", flush=True)
+
+
+@pytest.mark.parametrize("T", range(1, 9))
+def test_c1_decode_router_every_T(layers, T):
+    """Decode at C1 shapes through the router (no given logits) for every token count
+    1..8, without and with the residual: the single-token launch with its own selection,
+    the fused down + combine (<= 16 slots) and the separate combine (more slots)."""
+    dl = layers("c1")
+    cfg = dl.cfg
+    x = synth.gen_x(cfg, seed=100 + T, T=T)
+    outs = {}
+    for flags in (0, bq.MOE_ADD_RESIDUAL):
+        print(f"[c1-router] decode T={T} flags={flags}", flush=True)
+        outs[flags], rt = _run(dl, x, "decode", flags)
+        ref_logits = oracle.router_logits(x, synth.gen_router(cfg), synth.gen_bias(cfg))
+        assert_parity_f32(rt["logits"], ref_logits)
+        check_routing_exact(cfg, rt["logits"], rt)
+    slots = int((rt["counts"] > 0).sum()) + cfg.n_shared
+    print(f"  T={T}: {slots} slots ({'fused' if slots <= 16 else 'separate'} combine)", flush=True)
+    ref0, ref1 = oracle_outputs(cfg, 0, x, rt["logits"], np.arange(T), "both")
+    assert_parity(outs[0], ref0, f"c1 router T={T}")
+    assert_parity(outs[bq.MOE_ADD_RESIDUAL], ref1, f"c1 router T={T} residual")
+
+
+SMALL_ROUTER = synth.small_config(synth.CONFIGS["c0"], name="small_router", n_shared=1)
+
+
+def test_small_decode_router_every_T(layers):
+    """Decode at C0 shapes with a shared expert, through the router, T = 1..8, without
+    and with the residual (every slot list fits the fused down + combine)."""
+    dl = layers("small_router", SMALL_ROUTER)
+    cfg = dl.cfg
+    for T in range(1, 9):
+        x = synth.gen_x(cfg, seed=200 + T, T=T)
+        outs = {}
+        for flags in (0, bq.MOE_ADD_RESIDUAL):
+            print(f"[small-router] decode T={T} flags={flags}", flush=True)
+            outs[flags], rt = _run(dl, x, "decode", flags)
+            ref_logits = oracle.router_logits(x, synth.gen_router(cfg), synth.gen_bias(cfg))
+            assert_parity_f32(rt["logits"], ref_logits)
+            check_routing_exact(cfg, rt["logits"], rt)
+        ref0, ref1 = oracle_outputs(cfg, 0, x, rt["logits"], np.arange(T), "both")
+        assert_parity(outs[0], ref0, f"small router T={T}")
+        assert_parity(outs[bq.MOE_ADD_RESIDUAL], ref1, f"small router T={T} residual")
+
+
+@pytest.mark.parametrize("q", [synth.QT_INT2, synth.QT_TERNARY])
+@pytest.mark.parametrize("T", [37, 300])
+def test_prefill_router_ragged(layers, q, T):
+    """Prefill through the router (logits computed from x, several row blocks of the
+    logits kernel with a clamped last one) at token counts that are not multiples of 8,
+    with the residual; and moe_route_topk alone at the same T."""
+    cfg = synth.small_config(MULTI, name=f"prouter{q}", router=True, T=T, q_gate=q, q_up=q,
+                             q_down=q)
+    dl = layers(cfg.name, cfg)
+    x = synth.gen_x(cfg, seed=300 + T)
+    _full_check(dl, x, "prefill", flags=bq.MOE_ADD_RESIDUAL, label=f"prouter q={q} T={T}")
+    R = bq.alloc_routing(T, cfg.E, cfg.k, DEV)
+    ws = bq.alloc_workspace(dl.handle, T, DEV)
+    bq.moe_route_topk(dl.handle, _to_dev_u16(x), T, 0, R, ws)
+    torch.cuda.synchronize()
+    rt = _routing_host(R, T, cfg.k)
+    assert_parity_f32(rt["logits"], oracle.router_logits(x, synth.gen_router(cfg),
+                                                         synth.gen_bias(cfg)))
+    check_routing_exact(cfg, rt["logits"], rt)
 
 
 # ------------------------------------------------------------ edge cases

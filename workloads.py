@@ -23,18 +23,20 @@ def host_threads() -> int:
 
 
 def pack_expert(cfg: synth.Config, layer: int, e: int, out: np.ndarray | None = None,
-                seed: int | None = None, qtypes=None) -> np.ndarray:
+                seed: int | None = None, qtypes=None, mats=None) -> np.ndarray:
     """Packed gate|up|down blob of expert e (e == E is the shared expert).  With `qtypes`,
     a projection whose code family differs from cfg's is packed in cfg's family and then
-    re-quantised to the one given (moe_requantize): a lower-bit shadow copy."""
+    re-quantised to the one given (moe_requantize): a lower-bit shadow copy.  With `mats`,
+    mats(e) supplies the three (codes [N][K], scales [N][K/32]) instead of the generator."""
     qt = tuple(qtypes or cfg.qtypes)
     nbytes = bq.moe_expert_bytes(*qt, cfg.d, cfg.inter)
     if out is None:
         out = np.empty(nbytes, np.uint8)
     off = 0
+    given = mats(e) if mats is not None else None
     for m in range(3):
         K, N = synth.matrix_shape(cfg, m)
-        c, s = synth.gen_matrix(cfg, layer, e, m, seed)
+        c, s = given[m] if given is not None else synth.gen_matrix(cfg, layer, e, m, seed)
         nb = bq.moe_packed_bytes(qt[m], K, N)
         if qt[m] == cfg.qtypes[m]:
             bq.moe_pack_weights(qt[m], c, s, out[off:off + nb])
@@ -49,10 +51,11 @@ class DeviceLayer:
     """One layer's packed experts (+ shared expert, router, bias) in device memory."""
 
     def __init__(self, cfg: synth.Config, layer: int = 0, device="cuda", seed=None,
-                 experts_override=None, shadow_qtypes=None):
+                 experts_override=None, shadow_qtypes=None, mats=None):
         # with shadow_qtypes, the experts of `cfg` re-quantised to those code families (a
         # lower-bit copy selected per call through its own layer handle); self.cfg then
-        # carries the shadow's families and self.source_cfg the original ones
+        # carries the shadow's families and self.source_cfg the original ones.  `mats(e)`,
+        # if given, supplies every expert's (codes, scales) instead of the generator
         self.source_cfg = cfg
         if shadow_qtypes is not None:
             q = tuple(shadow_qtypes)
@@ -65,7 +68,8 @@ class DeviceLayer:
         src, qt = self.source_cfg, cfg.qtypes
 
         def work(e):
-            pack_expert(src, layer, e, host[e * self.stride:(e + 1) * self.stride], seed, qt)
+            pack_expert(src, layer, e, host[e * self.stride:(e + 1) * self.stride], seed, qt,
+                        mats)
 
         with ThreadPoolExecutor(host_threads()) as ex:
             list(ex.map(work, range(E)))
@@ -74,7 +78,7 @@ class DeviceLayer:
         self.experts = torch.from_numpy(host).to(device)
         self.shared = None
         if cfg.n_shared:
-            sh = pack_expert(src, layer, E, None, seed, qt)
+            sh = pack_expert(src, layer, E, None, seed, qt, mats)
             self.shared = torch.from_numpy(sh).to(device)
         self.router_w = None
         if cfg.router:
