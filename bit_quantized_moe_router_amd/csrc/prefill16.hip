@@ -52,12 +52,13 @@ __device__ __forceinline__ float silu16(float g) {
 // A lane's 32-bit code word holds two 32-groups' 8 levels each: group P
 // (0 or 1) in bits 8P .. 8P+7 (levels k = 0, 2, 4, 6 of the lane's eight) and
 // 16 + 8P .. (levels k = 1, 3, 5, 7), two bits per level, low bit first.
-// fp16 pair D (levels 2D, 2D+1) of the operand: magnitude m2 (both halves),
-// sign set where bit B of the level is clear (nw = ~word).
+// fp16 pair D (levels 2D, 2D+1) of the operand: the scale s2 (both halves),
+// negated where bit B of the level is clear (nw = ~word).  The sign bit is
+// flipped, not set, so that a negative scale gives +|s| for those levels.
 template <int P, int D, int B>
-__device__ __forceinline__ uint32_t sign_pair(uint32_t nw, uint32_t m2) {
+__device__ __forceinline__ uint32_t sign_pair(uint32_t nw, uint32_t s2) {
   constexpr int pos = 8 * P + 2 * D + B;  // the bit in the low half; the high half is +16
-  return ((nw << (15 - pos)) & 0x80008000u) | m2;
+  return ((nw << (15 - pos)) & 0x80008000u) ^ s2;
 }
 
 // ternary: u = 2 b1 + b0 in {0, 1, 2} -> -s, 0, +s (a level with b0 set is 0)

@@ -97,6 +97,10 @@ size_t moe_packed_bytes(int qtype, int64_t K, int64_t N);
 size_t moe_expert_bytes(int q_gate, int q_up, int q_down, int64_t d, int64_t inter);
 
 /* Pack one projection on the host.
+ * Source: the "Xolotl" repository card, README "Quick start" ("Get a model"),
+ * names the experts' code families (a mixed ternary / 2-bit / 3-bit
+ * quantisation); the pages give no storage layout, so the packed format
+ * above is this library's own, laid out for the matrix-core operands.
  *   codes  : host, [N][K] level indices (row n holds k = 0..K-1)
  *   scales : host, [N][K/32] fp16 bit patterns
  *   out    : host buffer of out_bytes >= moe_packed_bytes(qtype, K, N); the
@@ -193,6 +197,12 @@ typedef struct {           /* caller-allocated device buffers, written by the ca
 size_t moe_workspace_bytes(const moe_layer* L, int32_t T);
 
 /* Router, top-k, weights and permutation only (the first steps of the layer).
+ * Source: the "Xolotl" repository card, README "How it works, in one
+ * paragraph": a token's router asks for a few experts and only those are
+ * used.  The pages give no scoring function, normalisation or tie rule; the
+ * definition at the top of this header (fp32 logits, k largest with the lower
+ * index first on ties, softmax over the k selected, permutation stable in
+ * token order) is this library's reading.
  *   x   : device bf16 [T][d] (ignored under MOE_LOGITS_GIVEN)
  *   R   : all fields required; logits is written unless MOE_LOGITS_GIVEN
  *   ws  : device workspace of ws_bytes >= moe_workspace_bytes(L, T) */
@@ -201,6 +211,9 @@ moe_status moe_route_topk(const moe_layer* L, const uint16_t* x, int32_t T, uint
 
 /* The whole layer for 1..8 tokens (decode), bandwidth-bound kernels that
  * stream each selected expert's packed bytes once for all its tokens.
+ * Source: the "Xolotl" repository card, README "Latest" (an expert decoded
+ * once for all the tokens that chose it, at 4-8 tokens) and "Fast mode
+ * (DeepSeek-V4.1)" (decode speed is set by the expert bytes read per token).
  *   x   : device bf16 [T][d];  out : device bf16 [T][d], must not overlap x
  *   R   : routing outputs as in moe_route_topk
  * T outside 1..8 returns MOE_ERR_INVALID_ARG. */
@@ -209,7 +222,10 @@ moe_status moe_forward_decode(const moe_layer* L, const uint16_t* x, int32_t T, 
                               void* stream);
 
 /* The whole layer for any T >= 1 (prefill): matrix-core grouped GEMMs over
- * the permuted rows.  Arguments as for moe_forward_decode. */
+ * the permuted rows.  Arguments as for moe_forward_decode.
+ * Source: the "Xolotl" repository card, README "What one PC can do" (prefill
+ * throughput over prompts of thousands of tokens, where every expert sees many
+ * rows); the grouped-GEMM form is this library's design, not the pages'. */
 moe_status moe_forward_prefill(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
                                moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out,
                                void* stream);

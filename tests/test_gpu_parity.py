@@ -17,8 +17,8 @@ import bit_quantized_moe_router_amd as bq
 import oracle
 import synth
 import workloads
-from helpers import (assert_parity, check_routing_exact, oracle_outputs, shadow_mats,
-                     stratified_tokens)
+from helpers import (assert_parity, check_routing_exact, oracle_outputs, parity_stats,
+                     shadow_mats, stratified_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -373,14 +373,23 @@ def test_c3_prefill_stratified(layers):
     assert_parity(out[toks], ref, "c3 stratified out")
 
 
+# end-to-end relL1 bounds after each C4 layer: about twice the oracle's own spread
+C4_E2E_REL_L1 = (1e-3, 4e-3, 1e-2, 2e-2)
+
+
 @pytest.mark.timeout(900)
 def test_c4_stack_stratified_and_end_to_end(layers):
     """C4, four ternary layers with the residual, at full size.
 
     Per layer: routing bit-exact over all 16384 tokens, and a stratified sample reaching
     every 128-row tile of every active expert checked against the oracle fed this layer's
-    GPU input.  End to end: 128 tokens (the first, the last and random ones) carried through
-    all four layers by the oracle on its own outputs, compared with the GPU's last layer."""
+    GPU input (the parity criterion).  End to end: 128 tokens (the first, the last and
+    random ones) carried through all four layers by the oracle on its own outputs,
+    compared with the GPU after each layer.  The stack has no normalisation and amplifies
+    a one-ulp difference in a fraction of a layer's outputs about a hundredfold per layer:
+    the oracle against itself with 0.55 % of its layer-0 outputs moved by one ulp differs
+    by relL1 1.9e-3, 5.1e-3 and 8.5e-3 after layers 1-3 (tests/c4_sensitivity.py).  The
+    end-to-end figures are held to about twice that."""
     cfg = synth.CONFIGS["c4"]
     x = synth.gen_x(cfg)
     rng = np.random.default_rng(4)
@@ -404,7 +413,10 @@ def test_c4_stack_stratified_and_end_to_end(layers):
         ref = oracle_outputs(cfg, layer, x_cat, lg_cat, np.arange(len(x_cat)), True)
         assert_parity(out[toks], ref[: len(toks)], f"c4 layer {layer} per-layer")
         x_e2e = ref[len(toks):]
-        st = assert_parity(out[e2e_toks], x_e2e, f"c4 after layer {layer} end-to-end")
+        st = parity_stats(out[e2e_toks], x_e2e)
+        print(f"  end-to-end after layer {layer}: {st}", flush=True)
+        assert st["rel_l1"] <= C4_E2E_REL_L1[layer], (layer, st)
+        assert st["max_err_frac"] <= 2e-2, (layer, st)
         x = out  # next layer's input
         del dl
         torch.cuda.empty_cache()
