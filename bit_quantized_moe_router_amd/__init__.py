@@ -16,7 +16,7 @@ import torch  # load torch's HIP runtime first: libbqmoe.so binds to the same on
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbqmoe.so")
-ABI_VERSION = 2  # moe_abi_version() of the include/moe.h this binding follows
+ABI_VERSION = 3  # moe_abi_version() of the include/moe.h this binding follows
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_BAD_CODES, \
     MOE_ERR_DEVICE = range(6)
@@ -29,12 +29,13 @@ MOE_DECODE_STAGES_ALL = 15
 MOE_PREFILL_STAGE_ROUTE, MOE_PREFILL_STAGE_STAGE_X, MOE_PREFILL_STAGE_GATEUP, \
     MOE_PREFILL_STAGE_DOWN, MOE_PREFILL_STAGE_COMBINE = 1, 2, 4, 8, 16
 MOE_PREFILL_STAGES_ALL = 31
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 EXPORTED = ("moe_packed_bytes", "moe_expert_bytes", "moe_pack_weights", "moe_quantize_rtn",
             "moe_requantize", "moe_workspace_bytes",
             "moe_route_topk", "moe_forward_decode", "moe_forward_prefill",
-            "moe_forward_decode_stages", "moe_forward_prefill_stages", "moe_status_string",
-            "moe_abi_version")
+            "moe_forward_decode_stages", "moe_forward_prefill_stages",
+            "moe_forward_decode_noalloc", "moe_status_string", "moe_abi_version")
 
 
 class MoeError(RuntimeError):
@@ -94,8 +95,10 @@ def load():
     lib.moe_forward_prefill.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, vp]
     lib.moe_forward_decode_stages.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, u32, vp]
     lib.moe_forward_prefill_stages.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, sz, vp, u32, vp]
+    lib.moe_forward_decode_noalloc.argtypes = [L, vp, ctypes.c_int32, u32, R, vp, vp]
     for f in (lib.moe_route_topk, lib.moe_forward_decode, lib.moe_forward_prefill,
-              lib.moe_forward_decode_stages, lib.moe_forward_prefill_stages):
+              lib.moe_forward_decode_stages, lib.moe_forward_prefill_stages,
+              lib.moe_forward_decode_noalloc):
         f.restype = i32
     lib.moe_status_string.argtypes, lib.moe_status_string.restype = [i32], ctypes.c_char_p
     lib.moe_abi_version.argtypes, lib.moe_abi_version.restype = [], i32
@@ -252,6 +255,14 @@ def moe_forward_decode(layer: Layer, x, T: int, flags: int, routing: Routing, ws
                                    ctypes.byref(routing.c), _ptr(ws),
                                    0 if ws is None else ws.numel(), _ptr(out), _stream(stream))
     _check(st, "moe_forward_decode")
+
+
+def moe_forward_decode_noalloc(layer: Layer, x, T: int, flags: int, routing: Routing, out,
+                               stream=None):
+    """moe_forward_decode with the library's static device workspace (no ws argument)."""
+    st = load().moe_forward_decode_noalloc(ctypes.byref(layer.c), _ptr(x), T, flags,
+                                           ctypes.byref(routing.c), _ptr(out), _stream(stream))
+    _check(st, "moe_forward_decode_noalloc")
 
 
 def moe_forward_prefill(layer: Layer, x, T: int, flags: int, routing: Routing, ws, out,

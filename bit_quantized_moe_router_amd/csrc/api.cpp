@@ -82,9 +82,10 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // shared checks for the calls that take routing buffers
+// (ws_need: the workspace bytes the call requires; 0 = moe_workspace_bytes(L, T))
 static moe_status check_common(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
                                const moe_routing* R, const void* ws, size_t ws_bytes,
-                               bool need_experts) {
+                               bool need_experts, size_t ws_need = 0) {
   if (!layer_ok(L)) {
     if (!L) return MOE_ERR_INVALID_ARG;
     // distinguish plain invalid values from unsupported-but-meaningful shapes
@@ -118,7 +119,7 @@ static moe_status check_common(const moe_layer* L, const uint16_t* x, int32_t T,
         return MOE_ERR_INVALID_ARG;
     }
   }
-  if (!ws || ws_bytes < moe_workspace_bytes(L, T)) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < (ws_need ? ws_need : moe_workspace_bytes(L, T))) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
@@ -149,11 +150,16 @@ extern "C" moe_status moe_route_topk(const moe_layer* L, const uint16_t* x, int3
                                                                          : MOE_OK;
 }
 
-static moe_status decode_impl(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
-                              moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out,
-                              uint32_t mask, void* stream) {
+namespace bqmoe {
+// decode_ws_only: the workspace need only hold the decode layout (the
+// no-allocation entry point's fixed array), not moe_workspace_bytes
+moe_status decode_call(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                       moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out, uint32_t mask,
+                       void* stream, bool decode_ws_only) {
   if (T < 1 || T > MOE_MAX_DECODE_TOKENS) return MOE_ERR_INVALID_ARG;
-  moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, true);
+  if (decode_ws_only && !layer_ok(L)) return L ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG;
+  const size_t need = decode_ws_only ? decode_ws_layout(L, T).total : 0;
+  moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, true, need);
   if (st != MOE_OK) return st;
   if (T * L->top_k > kDecodeMaxRoutedRows || T * (L->top_k + L->n_shared) > kDecodeMaxRows ||
       L->d > kDecodeMaxDim || L->inter > kDecodeMaxDim || !decode_shape_ok(L, T))
@@ -164,6 +170,13 @@ static moe_status decode_impl(const moe_layer* L, const uint16_t* x, int32_t T, 
   const DecodeWs W = decode_ws_layout(L, T);
   return launch_decode(L, x, T, flags, R, (uint8_t*)ws, W, out, stream, mask) ? MOE_ERR_DEVICE
                                                                             : MOE_OK;
+}
+}  // namespace bqmoe
+
+static moe_status decode_impl(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                              moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out,
+                              uint32_t mask, void* stream) {
+  return decode_call(L, x, T, flags, R, ws, ws_bytes, out, mask, stream, false);
 }
 
 static moe_status prefill_impl(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
@@ -221,4 +234,4 @@ extern "C" const char* moe_status_string(moe_status s) {
   return "unknown status";
 }
 
-extern "C" int moe_abi_version(void) { return 2; }
+extern "C" int moe_abi_version(void) { return 3; }

@@ -96,6 +96,11 @@ bool prefill_exact16(const moe_layer* L);
 int prefill_tile_rows(const moe_layer* L);
 int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* R, uint8_t* ws,
                      const PrefillWs& P, void* stream, uint32_t mask);
+// moe_forward_decode's validation and dispatch; with decode_ws_only the workspace need only
+// hold decode_ws_layout(L, T) (the no-allocation entry point's fixed array).
+moe_status decode_call(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                       moe_routing* R, void* ws, size_t ws_bytes, uint16_t* out, uint32_t mask,
+                       void* stream, bool decode_ws_only);
 // out[t] = bf16([x[t]] + sum_j w[t][j] * y[inv_row[t][j]] + [y[T*k + t]]) for all T tokens
 int launch_combine(const uint16_t* y, int T, int d, int k, int n_shared, const int32_t* inv_row,
                    const float* w, const uint16_t* x, int residual, uint16_t* out, void* stream);

@@ -27,7 +27,9 @@
  *   - Device pointers are HIP device addresses; the caller owns and allocates
  *     every buffer (inputs, outputs and the workspace).  The library allocates
  *     nothing, keeps no pointer after returning and has no mutable global
- *     state; calls are thread-safe.
+ *     state; calls are thread-safe.  The one exception is
+ *     moe_forward_decode_noalloc, whose workspace is a static device array
+ *     of the library (see its comment).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
  *     on it and return without synchronising; argument errors are returned
  *     before anything is enqueued.  A failed launch returns MOE_ERR_DEVICE.
@@ -268,10 +270,33 @@ moe_status moe_forward_prefill_stages(const moe_layer* L, const uint16_t* x, int
                                       uint32_t flags, moe_routing* R, void* ws, size_t ws_bytes,
                                       uint16_t* out, uint32_t stage_mask, void* stream);
 
+/* ---------------------------------------------------------- no allocation
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): the same layer
+ * as moe_forward_decode, same kernels, arguments, validation and results,
+ * without the workspace argument.  The workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library; each GPU the library runs on
+ * holds its own copy until the process ends, and its address is looked up
+ * once per device, on the first call on that device.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ * Every call on one GPU uses that GPU's array: calls on one stream are
+ * ordered and safe, but calls whose work overlaps on one GPU (other streams,
+ * other host threads) race on it and must not be issued.  No kernel needs the
+ * array cleared between calls; each call writes all it reads.
+ * Errors: as moe_forward_decode; MOE_ERR_WORKSPACE if the decode workspace of
+ * (L, T) exceeds the array (no shape the decode path accepts does: d and
+ * inter <= 8192, T*k <= 64 need at most about 2.9 MB); MOE_ERR_DEVICE if the
+ * array's device address cannot be found. */
+enum { MOE_NOALLOC_SCRATCH_BYTES = 4 << 20 };
+moe_status moe_forward_decode_noalloc(const moe_layer* L, const uint16_t* x, int32_t T,
+                                      uint32_t flags, moe_routing* R, uint16_t* out,
+                                      void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 
-/* ABI version of this header: 2 (2 added the second expert copy to moe_layer). */
+/* ABI version of this header: 3 (2 added the second expert copy to moe_layer,
+ * 3 added moe_forward_decode_noalloc). */
 int moe_abi_version(void);
 
 #ifdef __cplusplus

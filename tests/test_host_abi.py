@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(bq.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert bq.moe_abi_version() == 2
+    assert bq.moe_abi_version() == 3
 
 
 def test_ceilings_library_exports_every_declared_symbol():
@@ -212,6 +212,23 @@ def test_decode_token_range():
     # 8 tokens x top-9 = 72 routed rows exceeds the decode kernels' 64
     L9 = _layer(n_experts=16, top_k=9)
     assert _call("moe_forward_decode", L9, 8) == bq.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_argument_checks():
+    # the token range and a missing layer or routing are refused before the device is
+    # looked up; on a host without a GPU the device lookup itself reports MOE_ERR_DEVICE
+    lib = bq.load()
+    L, R = _layer(), _routing()
+    f = lib.moe_forward_decode_noalloc
+    for T in (0, 9, -1):
+        assert f(ctypes.byref(L.c), FAKE, T, 0, ctypes.byref(R), FAKE + (1 << 30), None) == \
+            bq.MOE_ERR_INVALID_ARG
+    assert f(None, FAKE, 2, 0, ctypes.byref(R), FAKE + (1 << 30), None) == bq.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(L.c), FAKE, 2, 0, None, FAKE + (1 << 30), None) == bq.MOE_ERR_INVALID_ARG
+    import torch
+    if not torch.cuda.is_available():
+        assert f(ctypes.byref(L.c), FAKE, 2, 0, ctypes.byref(R), FAKE + (1 << 30), None) == \
+            bq.MOE_ERR_DEVICE
 
 
 def test_zero_tokens_is_a_noop():
