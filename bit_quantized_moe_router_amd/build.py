@@ -16,7 +16,7 @@ CEIL_SOURCES = ["ceilings.hip"]
 CEIL_LIB = os.path.join(HERE, "libbqceil.so")
 
 SOURCES = ["pack.cpp", "api.cpp", "route.hip", "decode.hip", "prefill.hip", "prefill16.hip",
-           "noalloc.hip"]
+           "prefill2x.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for every kernel: the scalar forms

@@ -49,8 +49,8 @@ PrefillWs prefill_ws_layout(const moe_layer* L, int T) {
   p.nblk = (T + kHistTokensPerBlock - 1) / kHistTokensPerBlock;
   const size_t rows_routed = (size_t)T * k;
   p.rows = (int)(rows_routed + (size_t)T * S);
-  p.max_tiles = (int)(rows_routed / kPrefillTileM + (size_t)E +
-                      (S ? ((size_t)T + kPrefillTileM - 1) / kPrefillTileM : 0));
+  const size_t tm = (size_t)prefill_tile_rows(L);
+  p.max_tiles = (int)(rows_routed / tm + (size_t)E + (S ? ((size_t)T + tm - 1) / tm : 0));
   size_t o = 0;
   p.ctrl = o;
   o = al256(o + 64);
@@ -70,6 +70,10 @@ PrefillWs prefill_ws_layout(const moe_layer* L, int T) {
   o = al256(o + 16 * (size_t)p.rows * (I / 32));
   p.y = o;
   o = al256(o + 2 * (size_t)p.rows * d);
+  p.x6 = o;
+  o = al256(o + (size_t)T * d);
+  p.h6 = o;
+  o = al256(o + (size_t)p.rows * I);
   p.total = o;
   return p;
 }
@@ -190,6 +194,10 @@ static moe_status prefill_impl(const moe_layer* L, const uint16_t* x, int32_t T,
   const size_t bytes = (size_t)T * L->d * 2;
   if (overlaps(x, bytes, out, bytes)) return MOE_ERR_INVALID_ARG;
   const PrefillWs P = prefill_ws_layout(L, T);
+  // the 2-bit kernels address their activation rows with 32-bit byte offsets
+  if (prefill_x2(L) && (size_t)P.rows * (size_t)(L->d > L->inter ? L->d : L->inter) * 2 >
+                           (size_t)UINT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
   return launch_prefill(L, x, T, flags, R, (uint8_t*)ws, P, out, stream, mask) ? MOE_ERR_DEVICE
                                                                              : MOE_OK;
 }

@@ -68,6 +68,8 @@ struct PrefillWs {
   size_t h;         // bf16 [rows][I]     h / 16
   size_t hsum;      // bf16 [rows][I/32][8] staged sums of h
   size_t y;         // bf16 [rows][d]
+  size_t x6;        // 2-bit layers: [T][d/32] 32-byte fp6 records of x's fp16 rows
+  size_t h6;        // 2-bit layers: [rows][I/32] 32-byte fp6 records of h's fp16 rows
   size_t total;
   int nblk, max_tiles, rows;
 };
@@ -96,6 +98,12 @@ bool prefill_exact16(const moe_layer* L);
 int prefill_tile_rows(const moe_layer* L);
 int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* R, uint8_t* ws,
                      const PrefillWs& P, void* stream, uint32_t mask);
+// Prefill of 2-bit layers on fp16 terms plus the fp6 x fp4 correction: the
+// stages after routing, on 128-row tiles of the tile list.
+bool prefill_x2(const moe_layer* L);
+int prefill_x2_tile_rows();
+int launch_prefill_x2(const moe_layer* L, const uint16_t* x, int T, moe_routing* R, uint8_t* ws,
+                      const PrefillWs& P, void* stream, uint32_t mask);
 // moe_forward_decode's validation and dispatch; with decode_ws_only the workspace need only
 // hold decode_ws_layout(L, T) (the no-allocation entry point's fixed array).
 moe_status decode_call(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,

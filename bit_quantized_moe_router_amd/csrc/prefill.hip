@@ -410,8 +410,9 @@ int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
     const int rc = launch_route_generic(L, x, T, flags, R, ws, P, stream);
     if (rc) return rc;
   }
-  if (prefill_exact16(L)) {
-    int rc = launch_prefill16(L, x, T, R, ws, P, stream, mask);
+  if (prefill_exact16(L) || prefill_x2(L)) {
+    int rc = prefill_exact16(L) ? launch_prefill16(L, x, T, R, ws, P, stream, mask)
+                                : launch_prefill_x2(L, x, T, R, ws, P, stream, mask);
     if (!rc && (mask & MOE_PREFILL_STAGE_COMBINE))
       rc = launch_combine((const uint16_t*)(ws + P.y), T, L->d, L->top_k, L->n_shared, R->inv_row,
                           R->topk_w, x, (flags & MOE_ADD_RESIDUAL) ? 1 : 0, out, stream);

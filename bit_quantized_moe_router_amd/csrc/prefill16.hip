@@ -296,7 +296,10 @@ bool prefill_exact16(const moe_layer* L) {
   return L->q_gate == MOE_Q_TERNARY && L->q_up == MOE_Q_TERNARY && L->q_down == MOE_Q_TERNARY;
 }
 
-int prefill_tile_rows(const moe_layer* L) { return prefill_exact16(L) ? kRows16 : kPrefillTileM; }
+int prefill_tile_rows(const moe_layer* L) {
+  if (prefill_x2(L)) return prefill_x2_tile_rows();
+  return prefill_exact16(L) ? kRows16 : kPrefillTileM;
+}
 
 static ProjDesc proj16(const moe_layer* L, int m) {
   const int K = m < 2 ? L->d : L->inter, N = m < 2 ? L->inter : L->d;

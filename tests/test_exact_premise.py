@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synth
-from exact_inputs import basis_tokens, check_premise, exact_mats
+from exact_inputs import PROJ, basis_tokens, check_premise, exact_mats
 
 from test_gpu_exact import DECODE_PATTERNS, FAMILIES, FULL, SMALL, _skewed_experts
 
@@ -31,3 +31,19 @@ def test_premise_full_shapes(qt):
     experts = _skewed_experts(cfg.E, cfg.T, seed=10)
     keep = np.arange(0, cfg.T, 16)
     check_premise(cfg, mats, x[keep], experts[keep])
+
+
+@pytest.mark.parametrize("odd", PROJ)
+def test_premise_odd_scales(odd):
+    small = synth.small_config(SMALL, q_gate=2, q_up=2, q_down=2)
+    x, _ = basis_tokens(small.d, small.T, seed=7, positions=(np.arange(small.T) * 37) % small.d)
+    check_premise(small, exact_mats(small, odd=odd), x, _skewed_experts(small.E, small.T, seed=8))
+    full = synth.small_config(FULL, q_gate=2, q_up=2, q_down=2)
+    mats = exact_mats(full, odd=odd)
+    for i in (0, 3, 8):
+        x, _ = basis_tokens(full.d, len(DECODE_PATTERNS[i]), seed=2000 + i)
+        check_premise(full, mats, x, np.array(DECODE_PATTERNS[i]))
+    x, _ = basis_tokens(full.d, full.T, seed=9)
+    experts = _skewed_experts(full.E, full.T, seed=10)
+    keep = np.arange(0, full.T, 16)
+    check_premise(full, mats, x[keep], experts[keep])

@@ -10,6 +10,9 @@ family in every projection position, decode slots of 1..8 rows (single-token
 launch, banded and per-group multi-row paths, fused and separate combine) at
 the full 4096/2048 shapes, and prefill row tiles that are full, ragged and
 multiple per expert at small and full shapes (2-bit/3-bit and ternary GEMMs).
+The odd-scale variants put 11-bit scales in one projection of a 2-bit layer:
+there the prefill's fp16 weight terms are off by the rounding residual of
+0.75 s, and only an exact fp6 x fp4 correction gives the identical output.
 """
 import numpy as np
 import pytest
@@ -18,7 +21,7 @@ import torch
 import bit_quantized_moe_router_amd as bq
 import synth
 import workloads
-from exact_inputs import basis_tokens, check_premise, exact_mats, top1_logits
+from exact_inputs import PROJ, basis_tokens, check_premise, exact_mats, top1_logits
 from helpers import oracle_outputs, parity_stats
 
 pytestmark = pytest.mark.gpu
@@ -43,9 +46,10 @@ def _skewed_experts(E, T, seed):
     return rng.choice(E, T, p=p / p.sum())
 
 
-def _layer(cfg, qt):
-    c = synth.small_config(cfg, name=f"{cfg.name}_{qt}", q_gate=qt[0], q_up=qt[1], q_down=qt[2])
-    mats = exact_mats(c)
+def _layer(cfg, qt, odd=""):
+    c = synth.small_config(cfg, name=f"{cfg.name}_{qt}{odd}", q_gate=qt[0], q_up=qt[1],
+                           q_down=qt[2])
+    mats = exact_mats(c, odd=odd)
     print(f"building exact layer {c.name}", flush=True)
     return c, mats, workloads.DeviceLayer(c, 0, DEV, mats=mats)
 
@@ -109,3 +113,32 @@ def test_exact_prefill_full_shapes(qt):
     print(f"  rows per expert {counts.tolist()}", flush=True)
     ref = oracle_outputs(cfg, 0, x, lg, np.arange(cfg.T), False, mats=mats)
     _assert_identical(out, ref, f"prefill full {qt}")
+
+
+@pytest.mark.parametrize("odd", PROJ)
+def test_exact_odd_scales_prefill(odd):
+    for cfg, seeds in ((SMALL, (7, 8)), (FULL, (9, 10))):
+        c, mats, dl = _layer(cfg, (2, 2, 2), odd)
+        pos = (np.arange(c.T) * 37) % c.d if cfg is SMALL else None
+        x, _ = basis_tokens(c.d, c.T, seed=seeds[0], positions=pos)
+        experts = _skewed_experts(c.E, c.T, seed=seeds[1])
+        lg = top1_logits(experts, c.E)
+        print(f"[exact prefill odd {odd} scales] {c.name} T={c.T}", flush=True)
+        out, counts = _run(dl, x, lg, "prefill")
+        print(f"  rows per expert {counts.tolist()}", flush=True)
+        ref = oracle_outputs(c, 0, x, lg, np.arange(c.T), False, mats=mats)
+        _assert_identical(out, ref, f"prefill odd {odd} {c.name}")
+
+
+@pytest.mark.parametrize("odd", PROJ)
+def test_exact_odd_scales_decode(odd):
+    cfg, mats, dl = _layer(FULL, (2, 2, 2), odd)
+    for i in (0, 3, 8):
+        pat = DECODE_PATTERNS[i]
+        experts = np.array(pat)
+        x, _ = basis_tokens(cfg.d, len(pat), seed=2000 + i)
+        lg = top1_logits(experts, cfg.E)
+        print(f"[exact decode odd {odd} scales] T={len(pat)} experts={pat}", flush=True)
+        out, _ = _run(dl, x, lg, "decode")
+        ref = oracle_outputs(cfg, 0, x, lg, np.arange(len(pat)), False, mats=mats)
+        _assert_identical(out, ref, f"decode odd {odd} T={len(pat)}")
