@@ -190,12 +190,13 @@ static moe_status prefill_impl(const moe_layer* L, const uint16_t* x, int32_t T,
   moe_status st = check_common(L, x, T, flags, R, ws, ws_bytes, true);
   if (st != MOE_OK) return st;
   if (L->alt_experts) return MOE_ERR_UNSUPPORTED;  // the second expert copy is read by decode
+  if (L->d % 256) return MOE_ERR_UNSUPPORTED;  // the down GEMMs cover 256 columns per block
   if (!out || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
   const size_t bytes = (size_t)T * L->d * 2;
   if (overlaps(x, bytes, out, bytes)) return MOE_ERR_INVALID_ARG;
   const PrefillWs P = prefill_ws_layout(L, T);
-  // the 2-bit kernels address their activation rows with 32-bit byte offsets
-  if (prefill_x2(L) && (size_t)P.rows * (size_t)(L->d > L->inter ? L->d : L->inter) * 2 >
+  // the 2-bit and ternary kernels address their activation rows with 32-bit byte offsets
+  if ((prefill_x2(L) || prefill_exact16(L)) && (size_t)P.rows * (size_t)(L->d > L->inter ? L->d : L->inter) * 2 >
                            (size_t)UINT32_MAX)
     return MOE_ERR_UNSUPPORTED;
   return launch_prefill(L, x, T, flags, R, (uint8_t*)ws, P, out, stream, mask) ? MOE_ERR_DEVICE

@@ -19,8 +19,12 @@
 // columns, with 4 waves:
 //   gate/up: wave w covers columns [32 (4c + w), +32) of gate and of up;
 //   down:    wave w covers columns [64 (4c + w), +64) (two column tiles).
+// Two blocks share a CU.  (One 8-wave block per CU, which stages a tile's
+// activations once per 512 columns instead of 256 and so halves their L2
+// traffic, measured 11% slower: independent blocks do not meet at the same
+// barriers, so one block's waves compute while the other's wait.)
 // Per 128-wide k-block the block stages the 128 rows' fp16 activations in
-// LDS with direct global->LDS loads (double-buffered), and each wave reads
+// LDS with direct-to-LDS buffer loads (double-buffered), and each wave reads
 // its packed tiles straight into registers one k-block ahead.
 #include <hip/hip_runtime.h>
 
@@ -34,9 +38,9 @@ typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRows16 = 128;                  // rows per tile
-constexpr int kCol16 = kRows16 * 16;          // one 16-byte chunk column of the tile
 constexpr int kBuf16 = kRows16 * 256;         // one k-block of activations
 constexpr int kDma16 = 16 * kRows16 / 64;     // direct loads per k-block (64 lanes x 16 B each)
+constexpr int kW16 = 4;                       // waves per block
 
 __device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256) void k_stage16(const uint16_t* src, int rows, 
 // column tiles).  A: fp16 rows (gather: tile row -> token through perm_tok),
 // rscale: 2^e of each source row.
 template <int NMAT>
-__global__ __launch_bounds__(256, 2) void k_pf16(
+__global__ __launch_bounds__(64 * kW16, 2) void k_pf16(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ tiles, const int32_t* __restrict__ ctrl,
     const int32_t* __restrict__ perm_tok, int Tk, int gather, const uint16_t* __restrict__ A,
@@ -155,11 +159,26 @@ __global__ __launch_bounds__(256, 2) void k_pf16(
     sScale[tid] = rscale[src];
   }
   __syncthreads();
-  const uint16_t* arow[2];
+  // LDS, per buffer: row R at R * 256, its 16-byte chunk c (8 k) in slot
+  // c ^ (R % 16).  A direct-to-LDS load writes 16 bytes per lane at
+  // consecutive slots, so 16 lanes fill one row's 256 bytes from 2 cache
+  // lines (with one row per lane, a load would touch 64 lines); the swizzle
+  // keeps the matrix-core reads (16 rows, one chunk) free of bank conflicts.
+  // Wave w loads rows 32w .. 32w + 31, four per load, with byte offsets into
+  // A from the buffer resource rA (the host bounds A below 4 GiB).
+  static_assert(kDma16 == 8 * kW16, "eight loads of 4 rows per wave");
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, -1, 0x00020000);
+  uint32_t aoffs[8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) arow[h] = A + (size_t)sTok[64 * h + lane] * K;
+  for (int i = 0; i < 8; ++i) {
+    const int R = 32 * wave + 4 * i + (lane >> 4);
+    aoffs[i] = (uint32_t)sTok[R] * (uint32_t)(2 * K) + (((lane & 15) ^ (R & 15)) << 4);
+  }
+  // matrix-core reads: chunk c = 4 GB + 2h + hl of row rt * 32 + l32 at
+  // l32 * 256 + (((4 GB + 2h) ^ ya) << 4) + rt * 8192
+  const uint32_t ya16 = (uint32_t)(hl ^ (l32 & 15)) << 4;
 
-  const int cw = col * 4 + wave;
+  const int cw = col * kW16 + wave;
   const uint8_t* const base0 = blob + pa.off;
   const uint8_t* const base1 = blob + pb.off;
   const size_t scl0 = pa.scales, scl1 = pb.scales;
@@ -179,18 +198,12 @@ __global__ __launch_bounds__(256, 2) void k_pf16(
   // column tile the lane's two 8-B code chunks and its column's 4 scales
   u32x2 cw_[2][2], cs_[2], nw_[2][2], ns_[2];
 
-  // chunk column c (8 k) of row R at c * kCol16 + R * 16: 32 rows of one
-  // matrix-core read are 512 contiguous bytes
 #define BQ16_ISSUE(KB_, BUF_)                                                                  \
   {                                                                                            \
-    uint8_t* dst = sbuf + (BUF_) * kBuf16;                                                     \
-    _Pragma("unroll") for (int i = 0; i < kDma16 / 4; ++i) {                                   \
-      const int ci = wave * (kDma16 / 4) + i; /* chunk column ci / 2, rows 64 (ci % 2) .. */   \
-      const uint16_t* src = arow[ci % 2] + (KB_) * 128 + (ci / 2) * 8;                         \
-      __builtin_amdgcn_global_load_lds((const void*)src,                                       \
-                                       (lds_void*)(dst + (ci / 2) * kCol16 + (ci % 2) * 1024), \
-                                       16, 0, 0);                                              \
-    }                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                              \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
+          rA, (lds_void*)(sbuf + (BUF_) * kBuf16 + (8 * wave + i) * 1024), 16, aoffs[i],       \
+          (KB_) * 256, 0, 0);                                                                  \
   }
 #define BQ16_LOADB(KB_, W_, S_)                                                                \
   {                                                                                            \
@@ -215,14 +228,15 @@ __global__ __launch_bounds__(256, 2) void k_pf16(
       BQ16_LOADB(kb + 1, nw_, ns_)
     }
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* sA = sbuf + buf * kBuf16;
+    const uint8_t* sA = sbuf + buf * kBuf16 + l32 * 256;
 
     // A fragments of group GB (8 reads of 16 B per lane)
 #define BQ16_READA(DST, GB)                                                                     \
-  _Pragma("unroll") for (int rt = 0; rt < 4; ++rt)                                              \
-      _Pragma("unroll") for (int h = 0; h < 2; ++h) DST[rt][h] =                                \
-          *reinterpret_cast<const u32x4*>(sA + ((GB) * 4 + 2 * h + hl) * kCol16 +              \
-                                          (rt * 32 + l32) * 16);
+  _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                               \
+    const uint8_t* pa_ = sA + (((4u * (GB) + 2u * h) << 4) ^ ya16);                              \
+    _Pragma("unroll") for (int rt = 0; rt < 4; ++rt) DST[rt][h] =                               \
+        *reinterpret_cast<const u32x4*>(pa_ + rt * 8192);                                       \
+  }
     // group GB on the fragments in aa; the next group's are read first, so
     // that their LDS latency runs under this group's matrix-core ops
 #define BQ16_GROUP(GB)                                                                          \
@@ -293,7 +307,8 @@ __global__ __launch_bounds__(256, 2) void k_pf16(
 
 // --------------------------------------------------------------- launchers
 bool prefill_exact16(const moe_layer* L) {
-  return L->q_gate == MOE_Q_TERNARY && L->q_up == MOE_Q_TERNARY && L->q_down == MOE_Q_TERNARY;
+  return L->q_gate == MOE_Q_TERNARY && L->q_up == MOE_Q_TERNARY && L->q_down == MOE_Q_TERNARY &&
+         L->inter % (32 * kW16) == 0 && L->d % (64 * kW16) == 0;
 }
 
 int prefill_tile_rows(const moe_layer* L) {
@@ -337,18 +352,20 @@ int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* 
     hipLaunchKernelGGL(k_stage16, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, xs, xscale);
   // grids: every (row tile, column group) item of the largest possible tile list
   if (mask & MOE_PREFILL_STAGE_GATEUP) {
-    const dim3 g1((unsigned)(((long)P.max_tiles * (I / 128) + 7) / 8 * 8));
-    hipLaunchKernelGGL(k_pf16<2>, g1, dim3(256), 0, s, experts, L->expert_stride, shared,
+    const int ncol = I / (32 * kW16);
+    const dim3 g1((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
+    hipLaunchKernelGGL(k_pf16<2>, g1, dim3(64 * kW16), 0, s, experts, L->expert_stride, shared,
                        proj16(L, 0), proj16(L, 1), tiles, ctrl, R->perm_tok, Tk, 1, xs, xscale, d,
-                       I, hs, I / 128);
+                       I, hs, ncol);
     // h to scaled fp16 rows in place, within this stage, so that every stage can be re-run
     hipLaunchKernelGGL(k_stage16, dim3((rows + 3) / 4), dim3(256), 0, s, hs, rows, I, hs, hscale);
   }
   if (mask & MOE_PREFILL_STAGE_DOWN) {
-    const dim3 g2((unsigned)(((long)P.max_tiles * (d / 256) + 7) / 8 * 8));
+    const int ncol = d / (64 * kW16);
+    const dim3 g2((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
     const ProjDesc pdn = proj16(L, 2);
-    hipLaunchKernelGGL(k_pf16<1>, g2, dim3(256), 0, s, experts, L->expert_stride, shared, pdn,
-                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hscale, I, d, y, d / 256);
+    hipLaunchKernelGGL(k_pf16<1>, g2, dim3(64 * kW16), 0, s, experts, L->expert_stride, shared, pdn,
+                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hscale, I, d, y, ncol);
   }
   return (int)hipGetLastError();
 }

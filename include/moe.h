@@ -224,9 +224,11 @@ moe_status moe_forward_decode(const moe_layer* L, const uint16_t* x, int32_t T, 
                               void* stream);
 
 /* The whole layer for any T >= 1 (prefill): matrix-core grouped GEMMs over
- * the permuted rows.  Arguments as for moe_forward_decode.  For a layer whose
- * three projections are all 2-bit, T * (top_k + n_shared) * max(d, inter) * 2
- * must not exceed 2^32 - 1 (MOE_ERR_UNSUPPORTED otherwise).
+ * the permuted rows.  Arguments as for moe_forward_decode.  d must be a
+ * multiple of 256 (MOE_ERR_UNSUPPORTED otherwise).  For a layer whose
+ * three projections are all 2-bit or all ternary,
+ * T * (top_k + n_shared) * max(d, inter) * 2 must not exceed 2^32 - 1
+ * (MOE_ERR_UNSUPPORTED otherwise).
  * Source: the "Xolotl" repository card, README "What one PC can do" (prefill
  * throughput over prompts of thousands of tokens, where every expert sees many
  * rows); the grouped-GEMM form is this library's design, not the pages'. */

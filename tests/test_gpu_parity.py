@@ -547,3 +547,17 @@ def test_zero_weights_give_shared_only(layers):
         mats = [synth.gen_matrix(cfg, 0, cfg.E, m) for m in range(3)]
         _, ysh = oracle.expert_rows(cfg.qtypes, mats, x)
         assert_parity(out, ysh, f"zero-{mode}")
+
+
+@pytest.mark.parametrize("q", [synth.QT_INT2, synth.QT_TERNARY])
+def test_prefill_refuses_d_not_multiple_of_256_decode_serves_it(q):
+    # d = 384: a valid layer (multiples of 128), which decode handles; the prefill
+    # GEMMs cover 256 output columns per block and refuse it
+    cfg = synth.small_config(synth.CONFIGS["c0"], name=f"d384_{q}", d=384, inter=256,
+                             q_gate=q, q_up=q, q_down=q)
+    dl = workloads.DeviceLayer(cfg, 0, DEV)
+    x = synth.gen_x(cfg)
+    with pytest.raises(bq.MoeError) as ei:
+        _run(dl, x, "prefill")
+    assert ei.value.status == bq.MOE_ERR_UNSUPPORTED
+    _full_check(dl, x, "decode", label="d384")
