@@ -83,12 +83,12 @@ def parse():
                          "times")
     ap.add_argument("--loop-stage", default="gateup", choices=["gateup", "down"],
                     help="the stage --kernel-loop launches")
-    ap.add_argument("--extra", default="c2,c2s,c4",
+    ap.add_argument("--extra", default="c2,c2s,c4,c1t",
                     help="further workloads measured after the headline ones and reported in "
                          "the same line: c2 (decode, 8 tokens), c2s (c2 through a 2-bit shadow "
-                         "of its 3-bit experts), c4 (4-layer prefill stack), c2m (c2 with its 64 "
-                         "most favoured experts read from a 2-bit copy; not run by default); "
-                         "'none' skips them")
+                         "of its 3-bit experts), c4 (4-layer prefill stack), c1t (c1 decode with "
+                         "ternary experts), c2m (c2 with its 64 most favoured experts read from "
+                         "a 2-bit copy; not run by default); 'none' skips them")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured roofline ceilings (read stream, matrix-core peak)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -108,6 +108,10 @@ def decode_leg(args, dev):
     import workloads
 
     cfg = synth.CONFIGS[args.config]
+    qts = getattr(args, "qtypes", None)
+    if qts is not None:  # the same shapes with other code families
+        cfg = synth.small_config(cfg, name=f"{cfg.name}_{'_'.join(synth_qname(q) for q in qts)}",
+                                 q_gate=qts[0], q_up=qts[1], q_down=qts[2])
     T, K, W, C = cfg.T, args.steps, args.warmup, max(1, args.copies)
     log(f"[decode] building {cfg.name} + {C - 1} device copies")
     shadow = getattr(args, "shadow", None)
@@ -249,7 +253,10 @@ def decode_leg(args, dev):
     roof = {"kernel": "k_dec_gateup (decode gate/up + SiLU)", "bound": "hbm",
             "achieved": gu_b / (gu_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": gu_b / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
-            "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_b}
+            "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_b,
+            "timing": "HIP events around back-to-back launches on the launch stream (includes "
+                      "the gaps between launches); the rocprofv3 kernel-trace average of the same "
+                      "command is kept under profiles/"}
     kernels = {"gateup_us": gu_us, "down_us": dn_us, "packed_expert_bytes": exp_b,
                "gbs": exp_b / ((gu_us + dn_us) * 1e-6) / 1e9,
                "frac": exp_b / ((gu_us + dn_us) * 1e-6) / 1e9 / HBM_PEAK_GBS}
@@ -449,7 +456,19 @@ def cpu_baseline(args, cfg, bytes_per_step, threads=1):
                       f"(logits, top-k, permutation, every active expert + shared, combine), "
                       f"{how} in double precision; {per_step * 1e3:.0f} ms per step; "
                       f"weight regeneration excluded",
-            "ms_per_step": per_step * 1e3, "host_cpus": os.cpu_count()}
+            "ms_per_step": per_step * 1e3, "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (what lscpu reports as 'Model name')."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -591,6 +610,19 @@ def extra_legs(args, dev):
         a = argparse.Namespace(**vars(args))
         a.prefill_config, a.prefill_steps = "c4", 2
         out["prefill_c4"] = prefill_leg(a, dev)
+    if "c1t" in want:
+        # single-token decode at c1's shapes with ternary experts (2 bits per code, as int2)
+        a = argparse.Namespace(**vars(args))
+        a.config, a.steps, a.warmup, a.copies, a.kernel_loop = "c1", 100, 10, 8, 0
+        a.qtypes = (1, 1, 1)
+        d = decode_leg(a, dev)
+        gbs = d["bytes_per_step"] / (d["ms"] * 1e-3) / 1e9
+        out["decode_c1_ternary"] = {
+            "workload": d["cfg"].name, "T": d["cfg"].T, "steps": a.steps, "layer_copies": a.copies,
+            "us_per_layer": d["ms"] * 1e3, "packed_expert_bytes_per_step": d["bytes_per_step"],
+            "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "gateup_kernel_us": d["roof"]["avg_launch_us"],
+            "gateup_kernel_gbs": d["roof"]["achieved"], "decode_kernels": d["kernels"]}
     return out
 
 
