@@ -339,8 +339,9 @@ def test_prefill_stages_one_by_one_and_rerun(layers, q):
         assert np.array_equal(_host_u16(out), full), st
 
 
-# Row-tile heights of the grouped GEMMs: 64-row tiles for 2-bit / 3-bit layers, 128-row tiles
-# for all-ternary layers.  The stratified samples reach every tile of these heights.
+# Row blocks the stratified samples reach: every 64-row block of the 2-bit layer (its grouped
+# GEMMs run 128-row tiles, so both halves of every tile; mixed 2-/3-bit layers run 64-row
+# tiles), and every 128-row tile of the all-ternary layers.
 TILE_ROWS_INT = 64
 TILE_ROWS_TERNARY = 128
 
@@ -357,7 +358,7 @@ def _assert_cover(cov, n_shared):
 @pytest.mark.timeout(600)
 def test_c3_prefill_stratified(layers):
     """C3 at full size: routing bit-exact over all 8192 tokens, and the output of a
-    stratified sample of >= 256 tokens whose rows reach every 64-row tile of every active
+    stratified sample of >= 256 tokens whose rows reach every 64-row block of every active
     expert (and every 64-token block of the shared expert) against the oracle."""
     dl = layers("c3")
     cfg = dl.cfg
