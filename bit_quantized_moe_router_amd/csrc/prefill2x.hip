@@ -94,7 +94,7 @@ __device__ __forceinline__ uint32_t e2m3_code(float t) {
 }
 
 // One wave per row of bf16 values: e = (exponent of max|v|) - 14, in
-// [-100, 114]; dst = fp16(v * 2^-e) (exact for the row's values down to 2^-32
+// [-100, 114]; dst = fp16(v * 2^-e) (exact for the row's values down to 2^-31
 // of its maximum), scale = 2^e, and per 32-group the record above, of the
 // values w = v * 2^-e with the group's scale 2^(floor(log2 max|w|) - 1)
 // (codes below 4).  src and dst may be the same rows: every element is read
