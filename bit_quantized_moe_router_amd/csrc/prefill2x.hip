@@ -98,7 +98,14 @@ __device__ __forceinline__ uint32_t e2m3_code(float t) {
 // of its maximum), scale = 2^e, and per 32-group the record above, of the
 // values w = v * 2^-e with the group's scale 2^(floor(log2 max|w|) - 1)
 // (codes below 4).  src and dst may be the same rows: every element is read
-// and rewritten by the same lane.
+// and rewritten by the same lane.  K is a multiple of 256.
+//
+// The second pass takes 8 consecutive values per lane (one 16-byte load and
+// store), so a 32-group spans 4 lanes: its maximum by two lane exchanges.  A
+// lane's 8 codes are record positions 8 jb .. 8 jb + 7, jb = (0, 2, 1, 3)[c]
+// for its chunk c of the group, in the order of k-slots (0, 4, 1, 5, 2, 6,
+// 3, 7) of the chunk (x_kslot); the group's chunk-0 lane gathers the four
+// 48-bit pieces and stores the record with two 16-byte stores.
 __global__ __launch_bounds__(256) void k_stage_x2(const uint16_t* src, int rows, int K,
                                                   uint16_t* dst, float* __restrict__ scale,
                                                   uint8_t* __restrict__ rec) {
@@ -118,34 +125,62 @@ __global__ __launch_bounds__(256) void k_stage_x2(const uint16_t* src, int rows,
   const int e = min(114, max(-100, (int)(m >> 7) - 127 - 14));
   const float f = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
   if (lane == 0) scale[row] = __uint_as_float((uint32_t)(127 + e) << 23);
-  // two groups per step, one per half-wave; lane j takes k-slot x_kslot(j)
-  const int half = lane >> 5, j = lane & 31, kk = x_kslot(j);
   uint8_t* rrow = rec + (size_t)row * (K / 32) * kRecX;
-  for (int g = half; g < K / 32; g += 2) {
-    const float w = bf16_to_f32(s[g * 32 + kk]) * f;
-    d[g * 32 + kk] = __builtin_bit_cast(uint16_t, (_Float16)w);
-    float gm = fabsf(w);
+  const int c = lane & 3;  // chunk of the lane's group
+  for (int i = lane * 8; i < K; i += 512) {  // the lanes of a group take the same trips
+    const uint4 v = *reinterpret_cast<const uint4*>(s + i);
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+    float w[8];
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o, 32));
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = bf16_to_f32(vw[j] & 0xFFFFu) * f;
+      w[2 * j + 1] = bf16_to_f32(vw[j] >> 16) * f;
+    }
+    uint4 o16;
+    uint32_t* o16w = reinterpret_cast<uint32_t*>(&o16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o16w[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w[2 * j]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w[2 * j + 1]) << 16);
+    *reinterpret_cast<uint4*>(d + i) = o16;
+    float gm = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gm = fmaxf(gm, fabsf(w[j]));
+    gm = fmaxf(gm, __shfl_xor(gm, 1, 4));
+    gm = fmaxf(gm, __shfl_xor(gm, 2, 4));
     // group scale 2^ea with max|w| / 2^ea in [2, 4); a zero group gets 2^-126
     int ea = (int)((__float_as_uint(gm) >> 23) & 0xFF) - 127 - 1;
     ea = max(-126, min(126, ea));
-    const uint32_t c = e2m3_code(w * __uint_as_float((uint32_t)(127 - ea) << 23));
-    // 4 codes -> 24 bits on lanes 4m, then 3 dwords on lanes 0 and 16
-    uint32_t p = c | ((uint32_t)__shfl_down((int)c, 1, 32) << 6);
-    p |= (uint32_t)__shfl_down((int)p, 2, 32) << 12;
-    const uint32_t p1 = (uint32_t)__shfl_down((int)p, 4, 32);
-    const uint32_t p2 = (uint32_t)__shfl_down((int)p, 8, 32);
-    const uint32_t p3 = (uint32_t)__shfl_down((int)p, 12, 32);
-    uint32_t* r32 = reinterpret_cast<uint32_t*>(rrow + (size_t)g * kRecX);
-    if (j == 0 || j == 16) {
-      const int o = j == 0 ? 0 : 3;
-      r32[o + 0] = (p & 0xFFFFFFu) | (p1 << 24);
-      r32[o + 1] = ((p1 >> 8) & 0xFFFFu) | (p2 << 16);
-      r32[o + 2] = ((p2 >> 16) & 0xFFu) | (p3 << 8);
+    const float inv = __uint_as_float((uint32_t)(127 - ea) << 23);
+    // the 8 codes in record order: k-slots 0, 4, 1, 5, 2, 6, 3, 7 of the chunk
+    uint64_t piece = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      piece |= (uint64_t)e2m3_code(w[(t >> 1) + 4 * (t & 1)] * inv) << (6 * t);
+    // record bytes 0..23 hold the pieces of chunks 0, 2, 1, 3 (jb = 0..3)
+    const int base = lane & ~3;
+    uint64_t pc[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const int from = base + (jb == 1 ? 2 : jb == 2 ? 1 : jb);
+      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)piece, from);
+      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(piece >> 32), from);
+      pc[jb] = (uint64_t)lo | ((uint64_t)hi << 32);
     }
-    if (j == 1) r32[6] = (uint32_t)(ea + 127);
-    if (j == 2) r32[7] = 0u;
+    if (c == 0) {
+      uint4 r0, r1;
+      r0.x = (uint32_t)pc[0];
+      r0.y = (uint32_t)(pc[0] >> 32) | ((uint32_t)pc[1] << 16);
+      r0.z = (uint32_t)(pc[1] >> 16);
+      r0.w = (uint32_t)pc[2];
+      r1.x = (uint32_t)(pc[2] >> 32) | ((uint32_t)pc[3] << 16);
+      r1.y = (uint32_t)(pc[3] >> 16);
+      r1.z = (uint32_t)(ea + 127);
+      r1.w = 0u;
+      uint8_t* rg = rrow + (size_t)(i / 32) * kRecX;
+      *reinterpret_cast<uint4*>(rg) = r0;
+      *reinterpret_cast<uint4*>(rg + 16) = r1;
+    }
   }
 }
 
