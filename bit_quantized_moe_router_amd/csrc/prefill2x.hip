@@ -44,6 +44,9 @@ namespace bqmoe {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRowsX = 128;                // rows per tile
@@ -238,11 +241,9 @@ __device__ __forceinline__ void tau_split(uint32_t w, uint32_t& g0, uint32_t& g1
   g1 = __builtin_amdgcn_perm(no, ne, 0x07050301u);
 }
 
-__device__ __forceinline__ i32x8 tau_operand(uint32_t w0, uint32_t w1, uint32_t sgn,
-                                             uint32_t keep) {
-  uint32_t a0, b0, a1, b1;
-  tau_split(w0, a0, b0);
-  tau_split(w1, a1, b1);
+// (from the two words' splits a0, b0 and a1, b1)
+__device__ __forceinline__ i32x8 tau_operand(uint32_t a0, uint32_t b0, uint32_t a1, uint32_t b1,
+                                             uint32_t sgn, uint32_t keep) {
   const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
   const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
   i32x8 r;
@@ -361,8 +362,12 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
   // of row rt * 32 + l32 at l32 * 256 + (((4 GB + 2h) ^ ya) << 4) + rt * 8192;
   // record half hf of group 2 gp + hl of that row at
   // l32 * 128 + (((4 gp + hf) ^ zr) << 4) + rt * 4096
-  const uint32_t ya16 = (uint32_t)(hl ^ (l32 & 15)) << 4;
-  const uint32_t zr16 = (uint32_t)((2 * hl) ^ ((l32 >> 1) & 7)) << 4;
+  // (the lane's parts: the XOR terms occupy bits 4..7, which no other term
+  // of an address touches, so a step's base takes them once and each read
+  // XORs in its chunk)
+  const uint32_t la16 = (uint32_t)(l32 * 256) | ((uint32_t)(hl ^ (l32 & 15)) << 4);
+  const uint32_t lr16 =
+      (uint32_t)(kStagesX * kA16X + l32 * 128) | ((uint32_t)((2 * hl) ^ ((l32 >> 1) & 7)) << 4);
 
   MainK mv = mk;
 #pragma unroll
@@ -371,18 +376,20 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
   const int cw = col * kWavesX + wave;
   const int KT = K / 128;  // packed tiles along K
   // packed weights, one buffer over the expert: the lane's two code words of
-  // column tile ct and k-half h at bw[ct][h] and its column's four scales at
-  // bs[ct], plus 512 (resp. 128) per tile along K
+  // column tile ct and k-half h at wu[ct] + 256 h + wl and its column's four
+  // scales at su[ct] + sl, plus 512 (resp. 128) per tile along K; the parts
+  // wu, su are the same for the whole wave (scalar offsets), wl, sl the
+  // lane's (one vector register each)
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)blob, 0, -1, kRsrcX);
-  uint32_t bw[2][2], bs[2];
+  const uint32_t wl = (uint32_t)((l32 >> 4) * KT * 512 + (16 * hl + r) * 8);
+  const uint32_t sl = (uint32_t)((l32 >> 4) * KT * 128 + r * 8);
+  uint32_t wu[2], su[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const bool sec = NMAT == 2 && ct == 1;
-    const uint32_t ntl = (uint32_t)((NMAT == 2 ? cw * 2 : cw * 4 + 2 * ct) + (l32 >> 4));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      bw[ct][h] = (uint32_t)(sec ? pb.off : pa.off) + ntl * KT * 512 + (16 * (2 * h + hl) + r) * 8;
-    bs[ct] = (uint32_t)(sec ? pb.off + pb.scales : pa.off + pa.scales) + ntl * KT * 128 + r * 8;
+    const uint32_t ntl = (uint32_t)(NMAT == 2 ? cw * 2 : cw * 4 + 2 * ct);
+    wu[ct] = (uint32_t)(sec ? pb.off : pa.off) + ntl * KT * 512;
+    su[ct] = (uint32_t)(sec ? pb.off + pb.scales : pa.off + pa.scales) + ntl * KT * 128;
   }
 
   f32x16 acc[kRtX][2];
@@ -408,10 +415,10 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
   {                                                                                            \
     _Pragma("unroll") for (int ct = 0; ct < 2; ++ct) {                                         \
       _Pragma("unroll") for (int h = 0; h < 2; ++h) W_[ct][h] =                                \
-          __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rB, (int)bw[ct][h],   \
-                                                                         (S_) * 512, 0));      \
+          __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(                      \
+                                        rB, (int)wl, (int)(wu[ct] + 256 * h + (S_) * 512), 0)); \
       SC_[ct] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(                \
-                                              rB, (int)bs[ct], (S_) * 128, 0));                \
+                                              rB, (int)sl, (int)(su[ct] + (S_) * 128), 0));    \
     }                                                                                          \
   }
 
@@ -440,17 +447,25 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
   };
   typedef u32x2 Words[2][2];
   typedef u32x2 Scales[2];
-  auto corr_ops = [&](auto gpc, const Words& w, const Scales& sc, Ops& o)
+  struct Split {
+    uint32_t a0, b0, a1, b1;  // tau_split of the column tile's two words
+  };
+  // the correction operands of column tile ct in two parts (split, then
+  // exchange, sign and scale), spread over the half's sub-steps
+  auto corr_split = [&](auto gpc, auto ctc, const Words& w, Split& sp)
       __attribute__((always_inline)) {
-    constexpr int gp = decltype(gpc)::value;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const uint32_t s16 = (sc[ct][gp] >> (16 * hl)) & 0xFFFFu;  // this lane's group is 2gp + hl
-      uint32_t e8, sgn, keep;
-      corr_scale(s16, e8, sgn, keep);
-      o.b4[ct] = tau_operand(w[ct][0][gp], w[ct][1][gp], sgn, keep);
-      o.sb[ct] = (int)e8;
-    }
+    constexpr int gp = decltype(gpc)::value, ct = decltype(ctc)::value;
+    tau_split(w[ct][0][gp], sp.a0, sp.b0);
+    tau_split(w[ct][1][gp], sp.a1, sp.b1);
+  };
+  auto corr_finish = [&](auto gpc, auto ctc, const Scales& sc, const Split& sp, Ops& o)
+      __attribute__((always_inline)) {
+    constexpr int gp = decltype(gpc)::value, ct = decltype(ctc)::value;
+    const uint32_t s16 = (sc[ct][gp] >> (16 * hl)) & 0xFFFFu;  // this lane's group is 2gp + hl
+    uint32_t e8, sgn, keep;
+    corr_scale(s16, e8, sgn, keep);
+    o.b4[ct] = tau_operand(sp.a0, sp.b0, sp.a1, sp.b1, sgn, keep);
+    o.sb[ct] = (int)e8;
   };
   auto bmain = [&](auto gpc, auto qc, const Words& w, const Scales& sc, u32x4 (&bm)[2])
       __attribute__((always_inline)) {
@@ -479,10 +494,11 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
       __builtin_amdgcn_sched_group_barrier(0x100, decltype(dc)::value, 0);
     }
   };
-  // sA: the stage's fp16 rows plus l32 * 256; c2 = 4 GB + 2h
-  auto loadA = [&](const uint8_t* sA, const uint32_t c2, u32x4 (&a)[kRtX])
+  // aS: the step's base of the lane's fp16 reads (la16 plus the stage);
+  // c2 = 4 GB + 2h
+  auto loadA = [&](const uint32_t aS, const uint32_t c2, u32x4 (&a)[kRtX])
       __attribute__((always_inline)) {
-    const uint8_t* p = sA + ((c2 << 4) ^ ya16);
+    const uint8_t* p = sbuf + (aS ^ (c2 << 4));
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) a[rt] = *reinterpret_cast<const u32x4*>(p + rt * 8192);
   };
@@ -494,62 +510,81 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
   };
   // half gp of a step: wc/sc its words, (wn, sn, gpn) those of the next half
   // (the same step's half 1, or the next step's half 0); bm0 holds the half's
-  // first weight operands on entry and the next half's on exit
-  auto half = [&](auto gpc, auto gpnc, const uint8_t* sA, const uint8_t* sR, const Words& wc,
-                  const Scales& sc, const Words& wn, const Scales& sn, u32x4 (&bm0)[2])
+  // first weight operands on entry and the next half's on exit.  A0 holds the
+  // first sub-step's activations on entry when PRE; with NEXT the half reads
+  // the next half's (same stage) into it during its correction ops.
+  auto half = [&](auto gpc, auto gpnc, auto prec, auto nextc, const uint32_t sA,
+                  const uint32_t sR, const Words& wc, const Scales& sc, const Words& wn,
+                  const Scales& sn, u32x4 (&bm0)[2], u32x4 (&A0)[kRtX])
       __attribute__((always_inline)) {
-    constexpr int gp = decltype(gpc)::value;
-    u32x4 A0[kRtX], A1[kRtX], bmx[2], bmy[2];
+    constexpr int gp = decltype(gpc)::value, gpn = decltype(gpnc)::value;
+    u32x4 A1[kRtX], bmx[2], bmy[2];
     Ops oc;
-    loadA(sA, 8 * gp, A0);
-    __builtin_amdgcn_sched_barrier(0);
-    // q0 (P 0, h 0): read q1, build q1
+    Split sp0, sp1;
+    if constexpr (!decltype(prec)::value) {
+      loadA(sA, 8 * gp, A0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // q0 (P 0, h 0): read q1, build q1 and split column tile 0's codes
     loadA(sA, 8 * gp + 2, A1);
     bmain(gpc, Q1{}, wc, sc, bmx);
+    corr_split(gpc, G0{}, wc, sp0);
     mfmas(A0, bm0);
-    pattern(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
+    pattern(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
-    // q1 (P 0, h 1): read q2, build q2 and the correction operands
+    // q1 (P 0, h 1): read q2, build q2 and split column tile 1's codes
     loadA(sA, 8 * gp + 4, A0);
     bmain(gpc, Q2{}, wc, sc, bmy);
-    corr_ops(gpc, wc, sc, oc);
+    corr_split(gpc, G1{}, wc, sp1);
     mfmas(A1, bmx);
-    pattern(std::integral_constant<int, 10>{}, std::integral_constant<int, 1>{});
+    pattern(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
-    // q2 (P 1, h 0): read q3, build q3
+    // q2 (P 1, h 0): read q3, build q3 and finish the correction operands
     loadA(sA, 8 * gp + 6, A1);
     bmain(gpc, Q3{}, wc, sc, bmx);
+    corr_finish(gpc, G0{}, sc, sp0, oc);
+    corr_finish(gpc, G1{}, sc, sp1, oc);
     mfmas(A0, bmy);
-    pattern(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
+    pattern(std::integral_constant<int, 7>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
     // q3 (P 1, h 1): read the records (group 2 gp + hl of each sub-tile),
     // build the next half's first weight operands
-    u32x4 R0[kRtX], R1[kRtX];
+    // (codes 0..15, codes 16..31 and the scale byte as three reads, so
+    // that the codes land in one register tuple)
+    i32x6 R6[kRtX];
+    uint32_t RS[kRtX];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      R0[rt] = *reinterpret_cast<const u32x4*>(sR + (((4u * gp) << 4) ^ zr16) + rt * 4096);
-      R1[rt] = *reinterpret_cast<const u32x4*>(sR + (((4u * gp + 1) << 4) ^ zr16) + rt * 4096);
+      const i32x4 c0 = *reinterpret_cast<const i32x4*>(sbuf + (sR ^ ((4u * gp) << 4)) + rt * 4096);
+      const uint8_t* p1 = sbuf + (sR ^ ((4u * gp + 1) << 4)) + rt * 4096;
+      const i32x2 c1 = *reinterpret_cast<const i32x2*>(p1);
+      R6[rt] = __builtin_shufflevector(c0, __builtin_shufflevector(c1, c1, 0, 1, -1, -1), 0, 1, 2,
+                                       3, 4, 5);
+      RS[rt] = *reinterpret_cast<const uint32_t*>(p1 + 8);
     }
     bmain(gpnc, Q0{}, wn, sn, bm0);
     mfmas(A1, bmx);
-    pattern(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
+    pattern(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
     __builtin_amdgcn_sched_barrier(0);
-    // the correction
+    // the correction; with NEXT, the next half's first activations meanwhile
+    if constexpr (decltype(nextc)::value) loadA(sA, 8 * gpn, A0);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      const i32x8 a6 = {(int)R0[rt][0], (int)R0[rt][1], (int)R0[rt][2], (int)R0[rt][3],
-                        (int)R1[rt][0], (int)R1[rt][1], 0, 0};
+      const i32x8 a6 = __builtin_shufflevector(R6[rt], i32x6{0, 0, 0, 0, 0, 0}, 0, 1, 2, 3, 4, 5,
+                                               6, 7);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
         acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a6, oc.b4[ct], acc[rt][ct], 2, 4, 0, (int)R1[rt][2], 0, oc.sb[ct]);
+            a6, oc.b4[ct], acc[rt][ct], 2, 4, 0, (int)RS[rt], 0, oc.sb[ct]);
     }
-    pattern(std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{});
+    pattern(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
   };
   Words wa, wb;
   Scales sa, sb2;
-  u32x4 bm0[2];
+  u32x4 bm0[2], A0[kRtX];
+  using F = std::false_type;
+  using T = std::true_type;
   BQX_ISSUE(0, 0)
   BQX_LOADB(0, wa, sa)
   BQX_ISSUE(min(1, S - 1), 1)
@@ -563,14 +598,18 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
     // lgkmcnt(0), then the barrier without a fence
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kDmaX, 0));
     __builtin_amdgcn_s_barrier();
+    // the first sub-step's activations are read before the loads are
+    // issued, so that the issue covers their latency
     const int st2 = st == 0 ? 2 : st - 1;  // (s + 2) % 3
+    const uint32_t sA = la16 + (uint32_t)(st * kA16X);
+    const uint32_t sR = lr16 + (uint32_t)(st * kA6X);
+    loadA(sA, 0, A0);
+    __builtin_amdgcn_sched_barrier(0);
     BQX_LOADB(min(s + 1, S - 1), nw_, ns_)
     BQX_ISSUE(min(s + 2, S - 1), st2)
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* sA = sbuf + st * kA16X + l32 * 256;
-    const uint8_t* sR = sbuf + kStagesX * kA16X + st * kA6X + l32 * 128;
-    half(G0{}, G1{}, sA, sR, cw_, cs_, cw_, cs_, bm0);
-    half(G1{}, G0{}, sA, sR, cw_, cs_, nw_, ns_, bm0);
+    half(G0{}, G1{}, T{}, T{}, sA, sR, cw_, cs_, cw_, cs_, bm0, A0);
+    half(G1{}, G0{}, T{}, F{}, sA, sR, cw_, cs_, nw_, ns_, bm0, A0);
     st = st == 2 ? 0 : st + 1;
   };
   for (int s = 0; s < S; s += 2) {  // S is even
