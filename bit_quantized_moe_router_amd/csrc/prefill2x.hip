@@ -509,43 +509,41 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
       for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mfma_f16x(a[rt], bm[ct], acc[rt][ct]);
   };
   // half gp of a step: wc/sc its words, (wn, sn, gpn) those of the next half
-  // (the same step's half 1, or the next step's half 0); bm0 holds the half's
-  // first weight operands on entry and the next half's on exit.  A0 holds the
-  // first sub-step's activations on entry when PRE; with NEXT the half reads
-  // the next half's (same stage) into it during its correction ops.
+  // (the same step's half 1, or the next step's half 0); bm0 and sp hold the
+  // half's first weight operands and its code splits on entry, and the next
+  // half's on exit.  A0 holds the first sub-step's activations on entry when
+  // PRE; with NEXT the half reads the next half's (same stage) into it during
+  // its correction ops.
   auto half = [&](auto gpc, auto gpnc, auto prec, auto nextc, const uint32_t sA,
                   const uint32_t sR, const Words& wc, const Scales& sc, const Words& wn,
-                  const Scales& sn, u32x4 (&bm0)[2], u32x4 (&A0)[kRtX])
+                  const Scales& sn, u32x4 (&bm0)[2], Split (&sp)[2], u32x4 (&A0)[kRtX])
       __attribute__((always_inline)) {
     constexpr int gp = decltype(gpc)::value, gpn = decltype(gpnc)::value;
     u32x4 A1[kRtX], bmx[2], bmy[2];
     Ops oc;
-    Split sp0, sp1;
     if constexpr (!decltype(prec)::value) {
       loadA(sA, 8 * gp, A0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // q0 (P 0, h 0): read q1, build q1 and split column tile 0's codes
+    // q0 (P 0, h 0): read q1, build q1
     loadA(sA, 8 * gp + 2, A1);
     bmain(gpc, Q1{}, wc, sc, bmx);
-    corr_split(gpc, G0{}, wc, sp0);
     mfmas(A0, bm0);
-    pattern(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
+    pattern(std::integral_constant<int, 4>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
-    // q1 (P 0, h 1): read q2, build q2 and split column tile 1's codes
+    // q1 (P 0, h 1): read q2, build q2 and column tile 0's correction operand
     loadA(sA, 8 * gp + 4, A0);
     bmain(gpc, Q2{}, wc, sc, bmy);
-    corr_split(gpc, G1{}, wc, sp1);
+    corr_finish(gpc, G0{}, sc, sp[0], oc);
     mfmas(A1, bmx);
     pattern(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
-    // q2 (P 1, h 0): read q3, build q3 and finish the correction operands
+    // q2 (P 1, h 0): read q3, build q3 and column tile 1's correction operand
     loadA(sA, 8 * gp + 6, A1);
     bmain(gpc, Q3{}, wc, sc, bmx);
-    corr_finish(gpc, G0{}, sc, sp0, oc);
-    corr_finish(gpc, G1{}, sc, sp1, oc);
+    corr_finish(gpc, G1{}, sc, sp[1], oc);
     mfmas(A0, bmy);
-    pattern(std::integral_constant<int, 7>{}, std::integral_constant<int, 1>{});
+    pattern(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
     // q3 (P 1, h 1): read the records (group 2 gp + hl of each sub-tile),
     // build the next half's first weight operands
@@ -566,8 +564,11 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
     mfmas(A1, bmx);
     pattern(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
     __builtin_amdgcn_sched_barrier(0);
-    // the correction; with NEXT, the next half's first activations meanwhile
+    // the correction; meanwhile the next half's code splits and, with NEXT,
+    // its first activations
     if constexpr (decltype(nextc)::value) loadA(sA, 8 * gpn, A0);
+    corr_split(gpnc, G0{}, wn, sp[0]);
+    corr_split(gpnc, G1{}, wn, sp[1]);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       const i32x8 a6 = __builtin_shufflevector(R6[rt], i32x6{0, 0, 0, 0, 0, 0}, 0, 1, 2, 3, 4, 5,
@@ -577,18 +578,21 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
         acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             a6, oc.b4[ct], acc[rt][ct], 2, 4, 0, (int)RS[rt], 0, oc.sb[ct]);
     }
-    pattern(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
+    pattern(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
   };
   Words wa, wb;
   Scales sa, sb2;
   u32x4 bm0[2], A0[kRtX];
+  Split sp[2];
   using F = std::false_type;
   using T = std::true_type;
   BQX_ISSUE(0, 0)
   BQX_LOADB(0, wa, sa)
   BQX_ISSUE(min(1, S - 1), 1)
   bmain(G0{}, Q0{}, wa, sa, bm0);
+  corr_split(G0{}, G0{}, wa, sp[0]);
+  corr_split(G0{}, G1{}, wa, sp[1]);
   int st = 0;  // ring stage of step s
   auto step = [&](const int s, const Words& cw_, const Scales& cs_, Words& nw_, Scales& ns_)
       __attribute__((always_inline)) {
@@ -608,8 +612,8 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
     BQX_LOADB(min(s + 1, S - 1), nw_, ns_)
     BQX_ISSUE(min(s + 2, S - 1), st2)
     __builtin_amdgcn_sched_barrier(0);
-    half(G0{}, G1{}, T{}, T{}, sA, sR, cw_, cs_, cw_, cs_, bm0, A0);
-    half(G1{}, G0{}, T{}, F{}, sA, sR, cw_, cs_, nw_, ns_, bm0, A0);
+    half(G0{}, G1{}, T{}, T{}, sA, sR, cw_, cs_, cw_, cs_, bm0, sp, A0);
+    half(G1{}, G0{}, T{}, F{}, sA, sR, cw_, cs_, nw_, ns_, bm0, sp, A0);
     st = st == 2 ? 0 : st + 1;
   };
   for (int s = 0; s < S; s += 2) {  // S is even
