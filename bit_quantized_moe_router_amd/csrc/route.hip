@@ -204,8 +204,8 @@ __device__ int block_exclusive_scan(int* a, int n, int* wave_tot) {
 //   2. the <= 64 selected rows sit one per lane of wave 0, which derives each
 //      row's in-expert rank, permuted position and slot from ~log2(E)
 //      ballots over the expert-id bits;
-//   3. every expert's count and offset is a count over the rows, held in
-//      registers.
+//   3. meanwhile, on waves 1..7, every expert's count and offset is a count
+//      over the rows, held in registers.
 // Slots list the active experts in ascending id, then the shared expert.
 constexpr int kSelThreads = 512;  // one wave per decode token
 
@@ -282,28 +282,30 @@ __global__ __launch_bounds__(kSelThreads) void k_dec_select(
       offsets[E] = rows;
       s_nact = n_active;
     }
+  } else {
+    // 3. meanwhile, on the other waves: every expert's count and offset, the
+    //    row ids in registers
+    int rid[kDecodeMaxRoutedRows];
+#pragma unroll
+    for (int q4 = 0; q4 < kDecodeMaxRoutedRows / 4; ++q4) {
+      const int4 v = *reinterpret_cast<const int4*>(s_row + 4 * q4);
+      rid[4 * q4] = 4 * q4 < rows ? v.x : 0x7FFFFFFF;
+      rid[4 * q4 + 1] = 4 * q4 + 1 < rows ? v.y : 0x7FFFFFFF;
+      rid[4 * q4 + 2] = 4 * q4 + 2 < rows ? v.z : 0x7FFFFFFF;
+      rid[4 * q4 + 3] = 4 * q4 + 3 < rows ? v.w : 0x7FFFFFFF;
+    }
+    for (int e = tid - 64; e < E; e += kSelThreads - 64) {
+      int cnt = 0, off = 0;
+#pragma unroll
+      for (int r = 0; r < kDecodeMaxRoutedRows; ++r) {
+        cnt += rid[r] == e;
+        off += rid[r] < e;
+      }
+      counts[e] = cnt;
+      offsets[e] = off;
+    }
   }
   __syncthreads();
-  // 3. every expert's count and offset, the row ids in registers
-  int rid[kDecodeMaxRoutedRows];
-#pragma unroll
-  for (int q4 = 0; q4 < kDecodeMaxRoutedRows / 4; ++q4) {
-    const int4 v = *reinterpret_cast<const int4*>(s_row + 4 * q4);
-    rid[4 * q4] = 4 * q4 < rows ? v.x : 0x7FFFFFFF;
-    rid[4 * q4 + 1] = 4 * q4 + 1 < rows ? v.y : 0x7FFFFFFF;
-    rid[4 * q4 + 2] = 4 * q4 + 2 < rows ? v.z : 0x7FFFFFFF;
-    rid[4 * q4 + 3] = 4 * q4 + 3 < rows ? v.w : 0x7FFFFFFF;
-  }
-  for (int e = tid; e < E; e += kSelThreads) {
-    int cnt = 0, off = 0;
-#pragma unroll
-    for (int r = 0; r < kDecodeMaxRoutedRows; ++r) {
-      cnt += rid[r] == e;
-      off += rid[r] < e;
-    }
-    counts[e] = cnt;
-    offsets[e] = off;
-  }
   // records past the last slot: no rows (a decode block reads only its own
   // record and stops on M == 0)
   const int n_slots = s_nact + (n_shared ? 1 : 0);

@@ -83,8 +83,8 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 // first sorts its PER entries by (key descending, index ascending); then each
 // of k rounds takes the largest head key of the wave, the lowest expert index
 // among the heads holding it (a second maximum, of inverted indices) and pops
-// that lane's head.  Every step runs in all lanes with vector operations only
-// (wave_allmax_u32), so a round is a short chain with no scalar round trips.
+// that lane's head (one ballot instead of the second maximum when a single
+// head holds the largest key).
 // Lanes 0..k-1 return the ids in order and their softmax weights
 // exp(l_j - l_0) / sum.  PER = entries per lane, a compile-time bound on E/64.
 template <int PER>
@@ -118,8 +118,17 @@ __device__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, i
   my_id = -1;
   for (int j = 0; j < k; ++j) {
     const uint32_t kmax = wave_allmax_u32(key[0]);
-    // lowest expert index among the heads equal to kmax: max of ~index
-    const uint32_t win = ~wave_allmax_u32(key[0] == kmax ? ~(uint32_t)ix[0] : 0u);
+    // The winner is the lowest expert index among the heads equal to kmax.
+    // When one lane's head holds kmax (the usual case) that head is it: a
+    // lane's entries are sorted, and every other head, hence every other
+    // entry, is smaller.  Otherwise a second maximum, of inverted indices,
+    // settles the tie (the branch is uniform over the wave).
+    const uint64_t at_max = __ballot(key[0] == kmax);
+    uint32_t win;
+    if (__popcll(at_max) == 1)
+      win = (uint32_t)__builtin_amdgcn_readlane(ix[0], (int)__ffsll((unsigned long long)at_max) - 1);
+    else
+      win = ~wave_allmax_u32(key[0] == kmax ? ~(uint32_t)ix[0] : 0u);
     const bool pop = (uint32_t)ix[0] == win;  // the winning lane pops its head
 #pragma unroll
     for (int t = 0; t + 1 < PER; ++t) {
