@@ -198,20 +198,31 @@ __global__ __launch_bounds__(256) void k_stage_x2(const uint16_t* src, int rows,
 // s * (u - 1.5) / 2 to nearest even.  The constants are kernel arguments; the
 // bases are copied into vector registers once (see Unpack2R), so that each
 // mask-and-or is a single v_and_or_b32 (a VOP3 op takes one scalar operand).
+// Parity 1's pair 0 sits at bit 8, inside the fp16 mantissa as it is: under
+// the base 2.0 the field is worth 1/2 per step, and one packed add of -2.75
+// gives (u - 1.5) / 2, without the shift.  (Pairs 0 and 1 share a base.)
 struct MainK {
   uint32_t msk[4], base[4], off[4];  // per pair: field mask, base bits, -(base/2 + 0.75)
+  uint32_t msk8, base8, off8;        // parity 1's pair 0 in place: mask, base 2.0, -2.75
 };
 
 template <int P>
 __device__ __forceinline__ u32x4 main_operand(uint32_t word, uint32_t s2, const MainK& mk) {
   const uint32_t x1 = P ? (word >> 8) : word;  // fields of pairs 0..3 at bits 0, 2, 4, 6
-  const uint32_t x0 = x1 << 2;                 // pair 0 at bit 2
   u32x4 r;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const uint32_t fv = ((v == 0 ? x0 : x1) & mk.msk[v]) | mk.base[v];
-    const f16x2 c = __builtin_bit_cast(f16x2, fv) * __builtin_bit_cast(f16x2, 0x38003800u) +
-                    __builtin_bit_cast(f16x2, mk.off[v]);
+    f16x2 c;
+    if (P == 1 && v == 0) {
+      const uint32_t fv = (word & mk.msk8) | mk.base8;
+      c = __builtin_bit_cast(f16x2, fv) + __builtin_bit_cast(f16x2, mk.off8);
+    } else {
+      // pair 0 of parity 0 moves up to bit 2 (at bit 0 the offset would not
+      // be an fp16 value)
+      const uint32_t fv = ((v == 0 ? word << 2 : x1) & mk.msk[v]) | mk.base[v == 0 ? 1 : v];
+      c = __builtin_bit_cast(f16x2, fv) * __builtin_bit_cast(f16x2, 0x38003800u) +
+          __builtin_bit_cast(f16x2, mk.off[v]);
+    }
     r[v] = __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(f16x2, s2));
   }
   return r;
@@ -268,6 +279,9 @@ __device__ __forceinline__ void corr_scale(uint32_t s16, uint32_t& e8, uint32_t&
   e8 = ((b >> 23) & 0xFFu) + 1u;  // 2|r|: the operand holds tau / 2
   sgn = (b >> 31) ? 0x88888888u : 0u;
   keep = r != 0.f ? 0xFFFFFFFFu : 0u;
+  // the mask as a register (an empty statement), so that each operand
+  // register takes one three-input bit op instead of a bit op and a select
+  __asm__("" : "+v"(keep));
 }
 
 __device__ __forceinline__ f32x16 mfma_f16x(u32x4 a, u32x4 b, f32x16 c) {
@@ -371,7 +385,8 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
 
   MainK mv = mk;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) mv.base[v] = lane_copy(mk.base[v]);
+  for (int v = 1; v < 4; ++v) mv.base[v] = lane_copy(mk.base[v]);
+  mv.base8 = lane_copy(mk.base8);
 
   const int cw = col * kWavesX + wave;
   const int KT = K / 128;  // packed tiles along K
@@ -683,6 +698,9 @@ static MainK main_constants() {
     k.base[v] = b[v];
     k.off[v] = o[v];
   }
+  k.msk8 = 0x03000300u;  // parity 1's pair 0 at bits 8-9 of each half
+  k.base8 = 0x40004000u;  // 2.0: the field adds u / 2
+  k.off8 = 0xC180C180u;   // -2.75
   return k;
 }
 
