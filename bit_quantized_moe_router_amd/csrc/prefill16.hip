@@ -34,7 +34,6 @@
 namespace bqmoe {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRows16 = 128;                  // rows per tile
@@ -56,29 +55,34 @@ __device__ __forceinline__ float silu16(float g) {
 // A lane's 32-bit code word holds two 32-groups' 8 levels each: group P
 // (0 or 1) in bits 8P .. 8P+7 (levels k = 0, 2, 4, 6 of the lane's eight) and
 // 16 + 8P .. (levels k = 1, 3, 5, 7), two bits per level, low bit first.
-// fp16 pair D (levels 2D, 2D+1) of the operand: the scale s2 (both halves),
-// negated where bit B of the level is clear (nw = ~word).  The sign bit is
-// flipped, not set, so that a negative scale gives +|s| for those levels.
-template <int P, int D, int B>
-__device__ __forceinline__ uint32_t sign_pair(uint32_t nw, uint32_t s2) {
-  constexpr int pos = 8 * P + 2 * D + B;  // the bit in the low half; the high half is +16
-  return ((nw << (15 - pos)) & 0x80008000u) ^ s2;
-}
+// fp16 pair D (levels 2D, 2D+1) of the operand is s * (u - 1) in both halves:
+// a mask-and-or puts the level u into the mantissa of a power-of-two base
+// where one step of the field is worth 1 (base 2^(10 - q) for a field at bit
+// q), one packed add of -(base + 1) gives u - 1 exactly, and one packed
+// multiply by the scale gives 0 or +-s, exact.  Group 1's fields sit at bits
+// 8, 10, 12, 14: pair 0 stays in place under base 4, the others are shifted
+// down by 8 onto group 0's positions.  The masks and offsets are kernel
+// arguments (scalar registers); the bases are copied into vector registers
+// once, so that each mask-and-or is one v_and_or_b32 (a VOP3 op takes one
+// scalar operand and no literal).
+struct TernK {
+  uint32_t msk[4], base[4], off[4];  // per pair D at bit 2D: mask, base 2^(10-2D), -(base+1)
+  uint32_t msk8, base8, off8;        // group 1's pair 0 at bit 8: mask, base 4, -5
+};
 
-// ternary: u = 2 b1 + b0 in {0, 1, 2} -> -s, 0, +s (a level with b0 set is 0)
-template <int P, int D>
-__device__ __forceinline__ uint32_t tern_pair(uint32_t nw, uint32_t s2) {
-  const uint32_t v = sign_pair<P, D, 1>(nw, s2);
-  const uint32_t nz = (nw >> (8 * P + 2 * D)) & 0x00010001u;  // 1 where b0 is clear
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v) * __builtin_bit_cast(u16x2, nz));
-}
-
-// The operand of one (group P of the word, k-half) of a lane.
 template <int P>
-__device__ __forceinline__ u32x4 build_tern(uint32_t word, uint32_t s2) {
-  const uint32_t nw = ~word;
-  return u32x4{tern_pair<P, 0>(nw, s2), tern_pair<P, 1>(nw, s2), tern_pair<P, 2>(nw, s2),
-               tern_pair<P, 3>(nw, s2)};
+__device__ __forceinline__ u32x4 build_tern(uint32_t word, uint32_t s2, const TernK& tk) {
+  const uint32_t x = P ? (word >> 8) : word;
+  u32x4 r;
+#pragma unroll
+  for (int D = 0; D < 4; ++D) {
+    const bool in_place = P == 1 && D == 0;
+    const uint32_t fv = in_place ? ((word & tk.msk8) | tk.base8) : ((x & tk.msk[D]) | tk.base[D]);
+    const f16x2 c = __builtin_bit_cast(f16x2, fv) +
+                    __builtin_bit_cast(f16x2, in_place ? tk.off8 : tk.off[D]);
+    r[D] = __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(f16x2, s2));
+  }
+  return r;
 }
 
 // ------------------------------------------------------------------ staging
@@ -130,7 +134,8 @@ __global__ __launch_bounds__(64 * kW16, 2) void k_pf16(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ tiles, const int32_t* __restrict__ ctrl,
     const int32_t* __restrict__ perm_tok, int Tk, int gather, const uint16_t* __restrict__ A,
-    const float* __restrict__ rscale, int K, int N, uint16_t* __restrict__ out, int ncol) {
+    const float* __restrict__ rscale, int K, int N, uint16_t* __restrict__ out, int ncol,
+    TernK tk) {
   __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * kBuf16];
   __shared__ int sTok[kRows16];
   __shared__ float sScale[kRows16];
@@ -175,16 +180,32 @@ __global__ __launch_bounds__(64 * kW16, 2) void k_pf16(
     aoffs[i] = (uint32_t)sTok[R] * (uint32_t)(2 * K) + (((lane & 15) ^ (R & 15)) << 4);
   }
   // matrix-core reads: chunk c = 4 GB + 2h + hl of row rt * 32 + l32 at
-  // l32 * 256 + (((4 GB + 2h) ^ ya) << 4) + rt * 8192
-  const uint32_t ya16 = (uint32_t)(hl ^ (l32 & 15)) << 4;
+  // l32 * 256 + (((4 GB + 2h) ^ ya) << 4) + rt * 8192; the lane's part la16
+  // (the XOR term occupies bits 4..7, which no other term touches, so a
+  // k-block's base takes it once and each read XORs in its chunk)
+  const uint32_t la16 = (uint32_t)(l32 * 256) | ((uint32_t)(hl ^ (l32 & 15)) << 4);
 
-  const int cw = col * kW16 + wave;
-  const uint8_t* const base0 = blob + pa.off;
-  const uint8_t* const base1 = blob + pb.off;
-  const size_t scl0 = pa.scales, scl1 = pb.scales;
-  int ntl[2];
+  TernK tv = tk;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) ntl[ct] = (NMAT == 2 ? cw * 2 : cw * 4 + 2 * ct) + (l32 >> 4);
+  for (int D = 0; D < 4; ++D) tv.base[D] = lane_copy(tk.base[D]);
+  tv.base8 = lane_copy(tk.base8);
+
+  // packed tiles, one buffer over the expert: the lane's two code chunks of
+  // column tile ct and k-half h at wu[ct] + 256 h + wl, its column's four
+  // scales at su[ct] + sl, plus 512 (resp. 128) per k-block; wu, su are the
+  // same for the whole wave (scalar offsets), wl, sl the lane's
+  const int cw = col * kW16 + wave;
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)blob, 0, -1, 0x00020000);
+  const uint32_t wl = (uint32_t)((l32 >> 4) * KB * 512 + (16 * hl + r) * 8);
+  const uint32_t sl = (uint32_t)((l32 >> 4) * KB * 128 + r * 8);
+  uint32_t wu[2], su[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const bool sec = NMAT == 2 && ct == 1;
+    const uint32_t ntl = (uint32_t)(NMAT == 2 ? cw * 2 : cw * 4 + 2 * ct);
+    wu[ct] = (uint32_t)(sec ? pb.off : pa.off) + ntl * KB * 512;
+    su[ct] = (uint32_t)(sec ? pb.off + pb.scales : pa.off + pa.scales) + ntl * KB * 128;
+  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -208,12 +229,11 @@ __global__ __launch_bounds__(64 * kW16, 2) void k_pf16(
 #define BQ16_LOADB(KB_, W_, S_)                                                                \
   {                                                                                            \
     _Pragma("unroll") for (int ct = 0; ct < 2; ++ct) {                                         \
-      const bool sec = NMAT == 2 && ct == 1;                                                   \
-      const uint8_t* bb = sec ? base1 : base0;                                                 \
-      const size_t tile_ = (size_t)ntl[ct] * KB + (KB_);                                       \
       _Pragma("unroll") for (int h = 0; h < 2; ++h) W_[ct][h] =                                \
-          *reinterpret_cast<const u32x2*>(bb + tile_ * 512 + (16 * (2 * h + hl) + r) * 8);    \
-      S_[ct] = *reinterpret_cast<const u32x2*>(bb + (sec ? scl1 : scl0) + tile_ * 128 + r * 8); \
+          __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(                      \
+                                        rB, (int)wl, (int)(wu[ct] + 256 * h + (KB_) * 512), 0)); \
+      S_[ct] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(                \
+                                              rB, (int)sl, (int)(su[ct] + (KB_) * 128), 0));   \
     }                                                                                          \
   }
 
@@ -228,12 +248,12 @@ __global__ __launch_bounds__(64 * kW16, 2) void k_pf16(
       BQ16_LOADB(kb + 1, nw_, ns_)
     }
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* sA = sbuf + buf * kBuf16 + l32 * 256;
+    const uint32_t aS = la16 + (uint32_t)(buf * kBuf16);
 
     // A fragments of group GB (8 reads of 16 B per lane)
 #define BQ16_READA(DST, GB)                                                                     \
   _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                               \
-    const uint8_t* pa_ = sA + (((4u * (GB) + 2u * h) << 4) ^ ya16);                              \
+    const uint8_t* pa_ = sbuf + (aS ^ ((4u * (GB) + 2u * h) << 4));                              \
     _Pragma("unroll") for (int rt = 0; rt < 4; ++rt) DST[rt][h] =                               \
         *reinterpret_cast<const u32x4*>(pa_ + rt * 8192);                                       \
   }
@@ -253,7 +273,7 @@ __global__ __launch_bounds__(64 * kW16, 2) void k_pf16(
     _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                             \
       u32x4 t[2];                                                                               \
       _Pragma("unroll") for (int ct = 0; ct < 2; ++ct)                                          \
-          t[ct] = build_tern<(GB) & 1>(((GB) < 2) ? cw_[ct][h][0] : cw_[ct][h][1], s2[ct]);     \
+          t[ct] = build_tern<(GB) & 1>(((GB) < 2) ? cw_[ct][h][0] : cw_[ct][h][1], s2[ct], tv); \
       _Pragma("unroll") for (int rt = 0; rt < 4; ++rt)                                          \
           _Pragma("unroll") for (int ct = 0; ct < 2; ++ct)                                      \
               acc[rt][ct] = mfma_f16(aa[rt][h], t[ct], acc[rt][ct]);                            \
@@ -330,6 +350,25 @@ static ProjDesc proj16(const moe_layer* L, int m) {
   return p;
 }
 
+static TernK tern_constants() {
+  // per pair D (field at bit q = 2D): the field's mask, the fp16 base
+  // 2^(10 - q) and -(base + 1), in both halves: 1024, 256, 64, 16 and -1025,
+  // -257, -65, -17; group 1's pair 0 at bit 8: base 4, -5
+  TernK k{};
+  const uint32_t m[4] = {0x00030003u, 0x000C000Cu, 0x00300030u, 0x00C000C0u};
+  const uint32_t b[4] = {0x64006400u, 0x5C005C00u, 0x54005400u, 0x4C004C00u};
+  const uint32_t o[4] = {0xE401E401u, 0xDC04DC04u, 0xD410D410u, 0xCC40CC40u};
+  for (int D = 0; D < 4; ++D) {
+    k.msk[D] = m[D];
+    k.base[D] = b[D];
+    k.off[D] = o[D];
+  }
+  k.msk8 = 0x03000300u;
+  k.base8 = 0x44004400u;
+  k.off8 = 0xC500C500u;
+  return k;
+}
+
 // The workspace areas of the bf16-operand path hold, here: xs the fp16 rows
 // of x, xsum their scales; h the bf16 h and then (by the end of the gate/up
 // stage) its fp16 rows, hsum their scales.
@@ -356,7 +395,7 @@ int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* 
     const dim3 g1((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
     hipLaunchKernelGGL(k_pf16<2>, g1, dim3(64 * kW16), 0, s, experts, L->expert_stride, shared,
                        proj16(L, 0), proj16(L, 1), tiles, ctrl, R->perm_tok, Tk, 1, xs, xscale, d,
-                       I, hs, ncol);
+                       I, hs, ncol, tern_constants());
     // h to scaled fp16 rows in place, within this stage, so that every stage can be re-run
     hipLaunchKernelGGL(k_stage16, dim3((rows + 3) / 4), dim3(256), 0, s, hs, rows, I, hs, hscale);
   }
@@ -365,7 +404,8 @@ int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* 
     const dim3 g2((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
     const ProjDesc pdn = proj16(L, 2);
     hipLaunchKernelGGL(k_pf16<1>, g2, dim3(64 * kW16), 0, s, experts, L->expert_stride, shared, pdn,
-                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hscale, I, d, y, ncol);
+                       pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hscale, I, d, y, ncol,
+                       tern_constants());
   }
   return (int)hipGetLastError();
 }
