@@ -101,6 +101,13 @@ int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* 
 // Prefill of 2-bit layers on fp16 terms plus the fp6 x fp4 correction: the
 // stages after routing, on 128-row tiles of the tile list.
 bool prefill_x2(const moe_layer* L);
+struct TernK;
+TernK tern_constants();
+// the 8-wave fp16-term GEMMs (prefill2x.hip) on an all-ternary layer, where
+// its shape allows (prefill_x2_shape); gate/up (mask bit GATEUP) or down
+int launch_pfx_tern(const moe_layer* L, int T, moe_routing* R, uint8_t* ws, const PrefillWs& P,
+                    void* stream, bool gateup);
+bool prefill_x2_shape(const moe_layer* L);
 int prefill_x2_tile_rows();
 int launch_prefill_x2(const moe_layer* L, const uint16_t* x, int T, moe_routing* R, uint8_t* ws,
                       const PrefillWs& P, void* stream, uint32_t mask);

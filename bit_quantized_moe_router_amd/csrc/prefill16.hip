@@ -51,40 +51,6 @@ __device__ __forceinline__ float silu16(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
-// ------------------------------------------------------------ operand build
-// A lane's 32-bit code word holds two 32-groups' 8 levels each: group P
-// (0 or 1) in bits 8P .. 8P+7 (levels k = 0, 2, 4, 6 of the lane's eight) and
-// 16 + 8P .. (levels k = 1, 3, 5, 7), two bits per level, low bit first.
-// fp16 pair D (levels 2D, 2D+1) of the operand is s * (u - 1) in both halves:
-// a mask-and-or puts the level u into the mantissa of a power-of-two base
-// where one step of the field is worth 1 (base 2^(10 - q) for a field at bit
-// q), one packed add of -(base + 1) gives u - 1 exactly, and one packed
-// multiply by the scale gives 0 or +-s, exact.  Group 1's fields sit at bits
-// 8, 10, 12, 14: pair 0 stays in place under base 4, the others are shifted
-// down by 8 onto group 0's positions.  The masks and offsets are kernel
-// arguments (scalar registers); the bases are copied into vector registers
-// once, so that each mask-and-or is one v_and_or_b32 (a VOP3 op takes one
-// scalar operand and no literal).
-struct TernK {
-  uint32_t msk[4], base[4], off[4];  // per pair D at bit 2D: mask, base 2^(10-2D), -(base+1)
-  uint32_t msk8, base8, off8;        // group 1's pair 0 at bit 8: mask, base 4, -5
-};
-
-template <int P>
-__device__ __forceinline__ u32x4 build_tern(uint32_t word, uint32_t s2, const TernK& tk) {
-  const uint32_t x = P ? (word >> 8) : word;
-  u32x4 r;
-#pragma unroll
-  for (int D = 0; D < 4; ++D) {
-    const bool in_place = P == 1 && D == 0;
-    const uint32_t fv = in_place ? ((word & tk.msk8) | tk.base8) : ((x & tk.msk[D]) | tk.base[D]);
-    const f16x2 c = __builtin_bit_cast(f16x2, fv) +
-                    __builtin_bit_cast(f16x2, in_place ? tk.off8 : tk.off[D]);
-    r[D] = __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(f16x2, s2));
-  }
-  return r;
-}
-
 // ------------------------------------------------------------------ staging
 // One wave per row of bf16 values: e = (exponent of max|v|) - 14, kept in
 // [-100, 114] so that 2^e and 2^-e are normal floats; every |v| * 2^-e is then
@@ -350,7 +316,7 @@ static ProjDesc proj16(const moe_layer* L, int m) {
   return p;
 }
 
-static TernK tern_constants() {
+TernK tern_constants() {
   // per pair D (field at bit q = 2D): the field's mask, the fp16 base
   // 2^(10 - q) and -(base + 1), in both halves: 1024, 256, 64, 16 and -1025,
   // -257, -65, -17; group 1's pair 0 at bit 8: base 4, -5
@@ -390,7 +356,14 @@ int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* 
   if (mask & MOE_PREFILL_STAGE_STAGE_X)
     hipLaunchKernelGGL(k_stage16, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, xs, xscale);
   // grids: every (row tile, column group) item of the largest possible tile list
-  if (mask & MOE_PREFILL_STAGE_GATEUP) {
+  // shapes that fit the 8-wave kernel (512 output columns per staged tile)
+  // run there, the rest on the 4-wave one
+  const bool wide = prefill_x2_shape(L);
+  if ((mask & MOE_PREFILL_STAGE_GATEUP) && wide) {
+    const int rc = launch_pfx_tern(L, T, R, ws, P, stream, true);
+    if (rc) return rc;
+    hipLaunchKernelGGL(k_stage16, dim3((rows + 3) / 4), dim3(256), 0, s, hs, rows, I, hs, hscale);
+  } else if (mask & MOE_PREFILL_STAGE_GATEUP) {
     const int ncol = I / (32 * kW16);
     const dim3 g1((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
     hipLaunchKernelGGL(k_pf16<2>, g1, dim3(64 * kW16), 0, s, experts, L->expert_stride, shared,
@@ -399,7 +372,10 @@ int launch_prefill16(const moe_layer* L, const uint16_t* x, int T, moe_routing* 
     // h to scaled fp16 rows in place, within this stage, so that every stage can be re-run
     hipLaunchKernelGGL(k_stage16, dim3((rows + 3) / 4), dim3(256), 0, s, hs, rows, I, hs, hscale);
   }
-  if (mask & MOE_PREFILL_STAGE_DOWN) {
+  if ((mask & MOE_PREFILL_STAGE_DOWN) && wide) {
+    const int rc = launch_pfx_tern(L, T, R, ws, P, stream, false);
+    if (rc) return rc;
+  } else if (mask & MOE_PREFILL_STAGE_DOWN) {
     const int ncol = d / (64 * kW16);
     const dim3 g2((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
     const ProjDesc pdn = proj16(L, 2);

@@ -307,14 +307,19 @@ __device__ __forceinline__ float silu_x(float g) {
 // and a vector-memory instruction per 7 matrix-core ops): with 256-row tiles
 // of 256 columns the traffic is half as large again and the L2, which the
 // activations are read from once per column group, becomes the bound.
-template <int NMAT>
+//
+// TERN: the same GEMM on an all-ternary layer, whose operands s * (u - 1)
+// are exact in fp16 (build_tern): no records, no correction ops, and the
+// product is the weight itself (no factor 2 in the epilogue).
+template <int NMAT, bool TERN = false>
 __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
     const uint8_t* __restrict__ experts, size_t stride, const uint8_t* __restrict__ shared,
     ProjDesc pa, ProjDesc pb, const int32_t* __restrict__ tiles, const int32_t* __restrict__ ctrl,
     const int32_t* __restrict__ perm_tok, int Tk, int gather, const uint16_t* __restrict__ A16,
     const float* __restrict__ rscale, const uint8_t* __restrict__ A6, int K, int N,
-    uint16_t* __restrict__ out, int ncol, MainK mk) {
+    uint16_t* __restrict__ out, int ncol, MainK mk, TernK tk) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sbuf[];  // kLdsX
+  constexpr int kDma = TERN ? kDmaA16X : kDmaX;  // direct loads per wave and k-step
 
   // work item = (row tile, column group), tile-major; each XCD takes one
   // contiguous chunk of the items (blocks go to the 8 XCDs round-robin), so
@@ -384,9 +389,16 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
       (uint32_t)(kStagesX * kA16X + l32 * 128) | ((uint32_t)((2 * hl) ^ ((l32 >> 1) & 7)) << 4);
 
   MainK mv = mk;
+  TernK tv = tk;
+  if constexpr (TERN) {
 #pragma unroll
-  for (int v = 1; v < 4; ++v) mv.base[v] = lane_copy(mk.base[v]);
-  mv.base8 = lane_copy(mk.base8);
+    for (int D = 0; D < 4; ++D) tv.base[D] = lane_copy(tk.base[D]);
+    tv.base8 = lane_copy(tk.base8);
+  } else {
+#pragma unroll
+    for (int v = 1; v < 4; ++v) mv.base[v] = lane_copy(mk.base[v]);
+    mv.base8 = lane_copy(mk.base8);
+  }
 
   const int cw = col * kWavesX + wave;
   const int KT = K / 128;  // packed tiles along K
@@ -421,7 +433,7 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
           rA, (lds_void*)(sbuf + (BUF_) * kA16X + (kDmaA16X * wave + i) * 1024), 16, aoffs[i], \
           (S_) * kKbX * 2, 0, 0);                                                              \
-    _Pragma("unroll") for (int i = 0; i < kDmaA6X; ++i)                                        \
+    _Pragma("unroll") for (int i = 0; i < (TERN ? 0 : kDmaA6X); ++i)                           \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
           rR, (lds_void*)(sbuf + kStagesX * kA16X + (BUF_) * kA6X + (kDmaA6X * wave + i) * 1024), \
           16, roffs[i], (S_) * 4 * kRecX, 0, 0);                                               \
@@ -442,9 +454,9 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
   // straight-line code).  The activations and records go through a ring of
   // three LDS stages with direct-to-LDS loads two steps ahead; the packed
   // words and scales go into registers one step ahead.  Per step a wave issues
-  // the words of step s + 1 and then the kDmaX direct loads of step s + 2; the
+  // the words of step s + 1 and then the kDma direct loads of step s + 2; the
   // memory counter counts in issue order, so at the top of step s a wait down
-  // to kDmaX outstanding loads leaves step s + 1's activations in flight.
+  // to kDma outstanding loads leaves step s + 1's activations in flight.
   // Loads beyond the last step repeat it (in bounds, into a stage no wave
   // reads any more), so that the step has no branch.  Unrolled by two, the
   // words of step s sit in one register set while those of step s + 1 load
@@ -489,7 +501,10 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const uint32_t sh = (sc[ct][gp] >> (16 * P)) & 0xFFFFu;
-      bm[ct] = main_operand<P>(w[ct][h][gp], sh | (sh << 16), mv);
+      if constexpr (TERN)
+        bm[ct] = build_tern<P>(w[ct][h][gp], sh | (sh << 16), tv);
+      else
+        bm[ct] = main_operand<P>(w[ct][h][gp], sh | (sh << 16), mv);
     }
   };
   auto kloop = [&](auto nrt_c) {
@@ -549,14 +564,14 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
     // q1 (P 0, h 1): read q2, build q2 and column tile 0's correction operand
     loadA(sA, 8 * gp + 4, A0);
     bmain(gpc, Q2{}, wc, sc, bmy);
-    corr_finish(gpc, G0{}, sc, sp[0], oc);
+    if constexpr (!TERN) corr_finish(gpc, G0{}, sc, sp[0], oc);
     mfmas(A1, bmx);
     pattern(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
     // q2 (P 1, h 0): read q3, build q3 and column tile 1's correction operand
     loadA(sA, 8 * gp + 6, A1);
     bmain(gpc, Q3{}, wc, sc, bmx);
-    corr_finish(gpc, G1{}, sc, sp[1], oc);
+    if constexpr (!TERN) corr_finish(gpc, G1{}, sc, sp[1], oc);
     mfmas(A0, bmy);
     pattern(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
@@ -567,7 +582,7 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
     i32x6 R6[kRtX];
     uint32_t RS[kRtX];
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
+    for (int rt = 0; rt < (TERN ? 0 : NRT); ++rt) {
       const i32x4 c0 = *reinterpret_cast<const i32x4*>(sbuf + (sR ^ ((4u * gp) << 4)) + rt * 4096);
       const uint8_t* p1 = sbuf + (sR ^ ((4u * gp + 1) << 4)) + rt * 4096;
       const i32x2 c1 = *reinterpret_cast<const i32x2*>(p1);
@@ -582,10 +597,12 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
     // the correction; meanwhile the next half's code splits and, with NEXT,
     // its first activations
     if constexpr (decltype(nextc)::value) loadA(sA, 8 * gpn, A0);
-    corr_split(gpnc, G0{}, wn, sp[0]);
-    corr_split(gpnc, G1{}, wn, sp[1]);
+    if constexpr (!TERN) {
+      corr_split(gpnc, G0{}, wn, sp[0]);
+      corr_split(gpnc, G1{}, wn, sp[1]);
+    }
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
+    for (int rt = 0; rt < (TERN ? 0 : NRT); ++rt) {
       const i32x8 a6 = __builtin_shufflevector(R6[rt], i32x6{0, 0, 0, 0, 0, 0}, 0, 1, 2, 3, 4, 5,
                                                6, 7);
 #pragma unroll
@@ -606,16 +623,18 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
   BQX_LOADB(0, wa, sa)
   BQX_ISSUE(min(1, S - 1), 1)
   bmain(G0{}, Q0{}, wa, sa, bm0);
-  corr_split(G0{}, G0{}, wa, sp[0]);
-  corr_split(G0{}, G1{}, wa, sp[1]);
+  if constexpr (!TERN) {
+    corr_split(G0{}, G0{}, wa, sp[0]);
+    corr_split(G0{}, G1{}, wa, sp[1]);
+  }
   int st = 0;  // ring stage of step s
   auto step = [&](const int s, const Words& cw_, const Scales& cs_, Words& nw_, Scales& ns_)
       __attribute__((always_inline)) {
     // k-step s is in LDS for every wave (the direct loads of step s + 1 may
     // remain in flight), and every wave is done reading the stage of step
-    // s - 1, which the loads of step s + 2 overwrite: vmcnt(kDmaX)
+    // s - 1, which the loads of step s + 2 overwrite: vmcnt(kDma)
     // lgkmcnt(0), then the barrier without a fence
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kDmaX, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kDma, 0));
     __builtin_amdgcn_s_barrier();
     // the first sub-step's activations are read before the loads are
     // issued, so that the issue covers their latency
@@ -661,7 +680,7 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
     for (int i = 0; i < 16; ++i) {
       const int m = rt * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
       if (m < M) {
-        const float sc = 2.0f * sScale[m];
+        const float sc = (TERN ? 1.0f : 2.0f) * sScale[m];
         if constexpr (NMAT == 2) {
           // gate and up of the same column of I: h = bf16(SiLU(g) * u)
           const float g = acc[rt][0][i] * sc, u = acc[rt][1][i] * sc;
@@ -677,12 +696,30 @@ __global__ __launch_bounds__(64 * kWavesX, 1) void k_pfx(
 }
 
 // --------------------------------------------------------------- launchers
+bool prefill_x2_shape(const moe_layer* L) {
+  return L->inter % (32 * kWavesX) == 0 && L->d % (64 * kWavesX) == 0;
+}
+
 bool prefill_x2(const moe_layer* L) {
   return L->q_gate == MOE_Q_INT2 && L->q_up == MOE_Q_INT2 && L->q_down == MOE_Q_INT2 &&
-         L->inter % (32 * kWavesX) == 0 && L->d % (64 * kWavesX) == 0;
+         prefill_x2_shape(L);
 }
 
 int prefill_x2_tile_rows() { return kRowsX;
+}
+
+// dynamic LDS above 64 KB, once per process, for every instantiation
+static bool pfx_lds_attributes() {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const void* fns[4] = {(const void*)k_pfx<2>, (const void*)k_pfx<1>, (const void*)k_pfx<2, true>,
+                          (const void*)k_pfx<1, true>};
+    for (const void* f : fns)
+      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsX) != hipSuccess)
+        return false;
+    attr_set = true;
+  }
+  return true;
 }
 
 static MainK main_constants() {
@@ -740,15 +777,7 @@ int launch_prefill_x2(const moe_layer* L, const uint16_t* x, int T, moe_routing*
   pdn.N = d;
   const MainK mk = main_constants();
   const size_t lds = (size_t)kLdsX;
-  static bool attr_set = false;  // dynamic LDS above 64 KB
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_pfx<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess ||
-        hipFuncSetAttribute((const void*)k_pfx<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
-      return (int)hipErrorInvalidConfiguration;
-    attr_set = true;
-  }
+  if (!pfx_lds_attributes()) return (int)hipErrorInvalidConfiguration;
   if (mask & MOE_PREFILL_STAGE_STAGE_X)
     hipLaunchKernelGGL(k_stage_x2, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, xs, xscale, x6);
   if (mask & MOE_PREFILL_STAGE_GATEUP) {
@@ -756,7 +785,7 @@ int launch_prefill_x2(const moe_layer* L, const uint16_t* x, int T, moe_routing*
     const dim3 g1((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
     hipLaunchKernelGGL(k_pfx<2>, g1, dim3(64 * kWavesX), lds, s, experts, L->expert_stride,
                        shared, pg, pu, tiles, ctrl, R->perm_tok, Tk, 1, xs, xscale, x6, d, I, hs,
-                       ncol, mk);
+                       ncol, mk, TernK{});
     // h to fp16 rows (in place) and records, within this stage, so that every
     // stage can be re-run
     hipLaunchKernelGGL(k_stage_x2, dim3((rows + 3) / 4), dim3(256), 0, s, hs, rows, I, hs,
@@ -767,7 +796,52 @@ int launch_prefill_x2(const moe_layer* L, const uint16_t* x, int T, moe_routing*
     const dim3 g2((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
     hipLaunchKernelGGL(k_pfx<1>, g2, dim3(64 * kWavesX), lds, s, experts, L->expert_stride,
                        shared, pdn, pdn, tiles, ctrl, R->perm_tok, Tk, 0, hs, hscale, h6, I, d, y,
-                       ncol, mk);
+                       ncol, mk, TernK{});
+  }
+  return (int)hipGetLastError();
+}
+
+// The GEMMs of an all-ternary layer on this kernel (prefill_x2_shape): the
+// staged fp16 rows of x (xs, xsum) or h (h, hsum) come from the ternary
+// staging kernel; gate/up writes bf16 h, down the rows of y.
+int launch_pfx_tern(const moe_layer* L, int T, moe_routing* R, uint8_t* ws, const PrefillWs& P,
+                    void* stream, bool gateup) {
+  hipStream_t s = (hipStream_t)stream;
+  const int k = L->top_k, d = L->d, I = L->inter;
+  const int Tk = T * k;
+  if (!pfx_lds_attributes()) return (int)hipErrorInvalidConfiguration;
+  const int32_t* tiles = (const int32_t*)(ws + P.tiles);
+  const int32_t* ctrl = (const int32_t*)(ws + P.ctrl);
+  const uint8_t* experts = (const uint8_t*)L->experts;
+  const uint8_t* shared = (const uint8_t*)L->shared;
+  const PackedLayout lg = packed_layout(MOE_Q_TERNARY, d, I);
+  const PackedLayout ld = packed_layout(MOE_Q_TERNARY, I, d);
+  ProjDesc pg{}, pu{}, pdn{};
+  pg.off = 0;
+  pu.off = lg.total;
+  pdn.off = 2 * lg.total;
+  pg.scales = pu.scales = lg.scales;
+  pdn.scales = ld.scales;
+  pg.qtype = pu.qtype = pdn.qtype = MOE_Q_TERNARY;
+  pg.K = pu.K = d;
+  pg.N = pu.N = I;
+  pdn.K = I;
+  pdn.N = d;
+  const TernK tk = tern_constants();
+  if (gateup) {
+    const int ncol = I / (32 * kWavesX);
+    const dim3 g1((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
+    hipLaunchKernelGGL((k_pfx<2, true>), g1, dim3(64 * kWavesX), kLdsX, s, experts,
+                       L->expert_stride, shared, pg, pu, tiles, ctrl, R->perm_tok, Tk, 1,
+                       (const uint16_t*)(ws + P.xs), (const float*)(ws + P.xsum), nullptr, d, I,
+                       (uint16_t*)(ws + P.h), ncol, MainK{}, tk);
+  } else {
+    const int ncol = d / (64 * kWavesX);
+    const dim3 g2((unsigned)(((long)P.max_tiles * ncol + 7) / 8 * 8));
+    hipLaunchKernelGGL((k_pfx<1, true>), g2, dim3(64 * kWavesX), kLdsX, s, experts,
+                       L->expert_stride, shared, pdn, pdn, tiles, ctrl, R->perm_tok, Tk, 0,
+                       (const uint16_t*)(ws + P.h), (const float*)(ws + P.hsum), nullptr, I, d,
+                       (uint16_t*)(ws + P.y), ncol, MainK{}, tk);
   }
   return (int)hipGetLastError();
 }
