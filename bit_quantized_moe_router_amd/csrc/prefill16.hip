@@ -19,13 +19,19 @@
 // columns, with 4 waves:
 //   gate/up: wave w covers columns [32 (4c + w), +32) of gate and of up;
 //   down:    wave w covers columns [64 (4c + w), +64) (two column tiles).
-// Two blocks share a CU.  (One 8-wave block per CU, which stages a tile's
-// activations once per 512 columns instead of 256 and so halves their L2
-// traffic, measured 11% slower: independent blocks do not meet at the same
-// barriers, so one block's waves compute while the other's wait.)
-// Per 128-wide k-block the block stages the 128 rows' fp16 activations in
-// LDS with direct-to-LDS buffer loads (double-buffered), and each wave reads
-// its packed tiles straight into registers one k-block ahead.
+// Two blocks share a CU.  Per 128-wide k-block the block stages the 128
+// rows' fp16 activations in LDS with direct-to-LDS buffer loads
+// (double-buffered), and each wave reads its packed tiles straight into
+// registers one k-block ahead.
+//
+// Layers whose inter is a multiple of 256 and d of 512 run their GEMMs on
+// the 8-wave kernel of the 2-bit path instead (k_pfx<NMAT, true> in
+// prefill2x.hip: one block per CU, 512 output columns per staged tile, a
+// three-stage ring whose waits leave the next step's loads in flight), with
+// the same operand build; this kernel serves the other shapes.  (An 8-wave
+// version of this kernel's own double-buffered loop was 11 % slower than two
+// 4-wave blocks: there the blocks' barriers, not the activation traffic, set
+// the time.)
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
