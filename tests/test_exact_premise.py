@@ -10,7 +10,7 @@ import pytest
 import synth
 from exact_inputs import PROJ, basis_tokens, check_premise, exact_mats
 
-from test_gpu_exact import DECODE_PATTERNS, FAMILIES, FULL, SMALL, _skewed_experts
+from test_gpu_exact import DECODE_PATTERNS, FAMILIES, FULL, NARROW, SMALL, _skewed_experts
 
 
 @pytest.mark.parametrize("qt", FAMILIES)
@@ -18,6 +18,13 @@ def test_premise_small_prefill(qt):
     cfg = synth.small_config(SMALL, q_gate=qt[0], q_up=qt[1], q_down=qt[2])
     x, _ = basis_tokens(cfg.d, cfg.T, seed=7, positions=(np.arange(cfg.T) * 37) % cfg.d)
     check_premise(cfg, exact_mats(cfg), x, _skewed_experts(cfg.E, cfg.T, seed=8))
+
+
+@pytest.mark.parametrize("qt", [(2, 2, 2), (1, 1, 1)])
+def test_premise_narrow_prefill(qt):
+    cfg = synth.small_config(NARROW, q_gate=qt[0], q_up=qt[1], q_down=qt[2])
+    x, _ = basis_tokens(cfg.d, cfg.T, seed=11, positions=(np.arange(cfg.T) * 41) % cfg.d)
+    check_premise(cfg, exact_mats(cfg), x, _skewed_experts(cfg.E, cfg.T, seed=12))
 
 
 @pytest.mark.parametrize("qt", [(2, 2, 2), (3, 3, 2)])

@@ -33,6 +33,10 @@ SMALL = synth.small_config(synth.CONFIGS["c3"], name="exact_small", T=700, d=512
                            inter=256, n_shared=1, router=False, zipf_s=0.0)
 FULL = synth.small_config(synth.CONFIGS["c3"], name="exact_full", T=256, E=16, k=1,
                           n_shared=1, router=False, zipf_s=0.0)
+# inter not a multiple of 256: all-ternary layers take the 4-wave fp16-term kernel and
+# 2-bit layers the bf16-operand kernel (the wider shapes above take the 8-wave one)
+NARROW = synth.small_config(synth.CONFIGS["c3"], name="exact_narrow", T=400, d=768, E=12, k=1,
+                            inter=384, n_shared=1, router=False, zipf_s=0.0)
 
 # decode routing patterns (token -> expert): slot heights 1..8 and a 9-slot list
 DECODE_PATTERNS = [[3], [5, 5], [1, 2, 1], [7, 7, 7, 7], [0, 0, 0, 0, 0], [2, 9, 9, 9, 9, 9],
@@ -100,6 +104,19 @@ def test_exact_prefill_small_reads_whole_matrices(qt):
     print(f"  rows per expert {counts.tolist()}", flush=True)
     ref = oracle_outputs(cfg, 0, x, lg, np.arange(cfg.T), False, mats=mats)
     _assert_identical(out, ref, f"prefill small {qt}")
+
+
+@pytest.mark.parametrize("qt", [(2, 2, 2), (1, 1, 1)])
+def test_exact_prefill_narrow_shapes(qt):
+    cfg, mats, dl = _layer(NARROW, qt)
+    x, _ = basis_tokens(cfg.d, cfg.T, seed=11, positions=(np.arange(cfg.T) * 41) % cfg.d)
+    experts = _skewed_experts(cfg.E, cfg.T, seed=12)
+    lg = top1_logits(experts, cfg.E)
+    print(f"[exact prefill narrow {qt}] T={cfg.T}", flush=True)
+    out, counts = _run(dl, x, lg, "prefill")
+    print(f"  rows per expert {counts.tolist()}", flush=True)
+    ref = oracle_outputs(cfg, 0, x, lg, np.arange(cfg.T), False, mats=mats)
+    _assert_identical(out, ref, f"prefill narrow {qt}")
 
 
 @pytest.mark.parametrize("qt", [(2, 2, 2), (3, 3, 2), (1, 1, 1)])
