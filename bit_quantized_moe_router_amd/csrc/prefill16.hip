@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "tern_operand.h"
 #include "moe_internal.h"
 
 namespace bqmoe {

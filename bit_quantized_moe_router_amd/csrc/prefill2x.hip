@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "tern_operand.h"
 #include "moe_internal.h"
 
 namespace bqmoe {
