@@ -29,10 +29,12 @@
 // Block: one 128-row tile of one expert and 8 waves (gate/up: wave w covers
 // 32 columns of gate and the same of up; down: 64 columns), so a tile's
 // activations are staged once per 256 (gate/up) or 512 (down) output
-// columns.  Per 64-wide k-step the block loads the fp16 rows (16 KB), their
-// fp6 records (8 KB) and its waves' packed words (10 KB) into a ring of three
-// LDS stages with direct-to-LDS buffer loads two steps ahead; each wave builds
-// both weight operands in registers.
+// columns.  Per 128-wide k-step the block loads the fp16 rows (32 KB) and
+// their fp6 records (16 KB) into a ring of three LDS stages with
+// direct-to-LDS buffer loads two steps ahead, and each wave its packed words
+// and scales into registers one step ahead; each wave builds both weight
+// operands in registers.  All-ternary layers of the same shapes run on the
+// same kernel (TERN): exact operands s * (u - 1), no records, no correction.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
