@@ -378,6 +378,76 @@ __global__ __launch_bounds__(256) void k_pf_combine(const uint16_t* __restrict__
   *reinterpret_cast<uint4*>(out + (size_t)t * d + c) = o;
 }
 
+// The same combine for a few tokens (decode): block = (256 columns, token), 4
+// columns per lane, so that T = 8 still spreads over 128 blocks; the token's
+// row indices and weights are uniform over the block (scalar loads).  Same
+// order of operations as k_pf_combine, so the same bits.
+__global__ __launch_bounds__(64) void k_combine_few(const uint16_t* __restrict__ y, int T, int d,
+                                                    int k, int n_shared,
+                                                    const int32_t* __restrict__ inv_row,
+                                                    const float* __restrict__ w,
+                                                    const uint16_t* __restrict__ x, int residual,
+                                                    uint16_t* __restrict__ out) {
+  const int t = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x * 4;
+  if (c >= d) return;  // d % 128 == 0: a lane's 4 columns are all in or all out
+  // the residual's load is issued first and converted last (x may be null
+  // without the residual: then row t of y stands in for it, unused)
+  const uint2 xv =
+      *reinterpret_cast<const uint2*>((residual ? x : y) + (size_t)t * d + c);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  bool first = true;
+  // rows in batches of 8: the batch's indices first, then all of its loads
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int rr[8];
+    float wt[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = min(j0 + jj, k - 1);
+      rr[jj] = inv_row[(size_t)t * k + j];
+      wt[jj] = w[(size_t)t * k + j];
+    }
+    // the weights' loads stay here, beside the indices' (the compiler would
+    // otherwise sink each into the branch below, one wait apiece)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) asm volatile("" : "+s"(wt[jj]));
+    uint2 yv[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      yv[jj] = *reinterpret_cast<const uint2*>(y + (size_t)rr[jj] * d + c);
+    if (first) {
+      // a = x (or 0), then a = fma(w_j, y_j, a) for j = 0, 1, ...: the order of
+      // k_pf_combine
+      if (residual) {
+        acc[0] = bf16_to_f32(xv.x & 0xFFFFu);
+        acc[1] = bf16_to_f32(xv.x >> 16);
+        acc[2] = bf16_to_f32(xv.y & 0xFFFFu);
+        acc[3] = bf16_to_f32(xv.y >> 16);
+      }
+      first = false;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < k) {
+        acc[0] = fmaf(wt[jj], bf16_to_f32(yv[jj].x & 0xFFFFu), acc[0]);
+        acc[1] = fmaf(wt[jj], bf16_to_f32(yv[jj].x >> 16), acc[1]);
+        acc[2] = fmaf(wt[jj], bf16_to_f32(yv[jj].y & 0xFFFFu), acc[2]);
+        acc[3] = fmaf(wt[jj], bf16_to_f32(yv[jj].y >> 16), acc[3]);
+      }
+    }
+  }
+  if (n_shared) {
+    const uint2 yv = *reinterpret_cast<const uint2*>(y + (size_t)(T * k + t) * d + c);
+    acc[0] += bf16_to_f32(yv.x & 0xFFFFu);
+    acc[1] += bf16_to_f32(yv.x >> 16);
+    acc[2] += bf16_to_f32(yv.y & 0xFFFFu);
+    acc[3] += bf16_to_f32(yv.y >> 16);
+  }
+  uint2 o;
+  o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+  o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+  *reinterpret_cast<uint2*>(out + (size_t)t * d + c) = o;
+}
+
 static ProjDesc proj_pf(const moe_layer* L, int m) {
   const int q = m == 0 ? L->q_gate : m == 1 ? L->q_up : L->q_down;
   const int K = m < 2 ? L->d : L->inter, N = m < 2 ? L->inter : L->d;
@@ -472,6 +542,11 @@ int launch_prefill(const moe_layer* L, const uint16_t* x, int T, uint32_t flags,
 
 int launch_combine(const uint16_t* y, int T, int d, int k, int n_shared, const int32_t* inv_row,
                    const float* w, const uint16_t* x, int residual, uint16_t* out, void* stream) {
+  if (T <= 64) {
+    hipLaunchKernelGGL(k_combine_few, dim3((unsigned)((d + 255) / 256), (unsigned)T), dim3(64), 0,
+                       (hipStream_t)stream, y, T, d, k, n_shared, inv_row, w, x, residual, out);
+    return (int)hipGetLastError();
+  }
   const long n = (long)T * (d / 8);
   hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      (hipStream_t)stream, y, T, d, k, n_shared, inv_row, w, x, residual, out);
