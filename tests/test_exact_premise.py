@@ -10,7 +10,8 @@ import pytest
 import synth
 from exact_inputs import PROJ, basis_tokens, check_premise, exact_mats
 
-from test_gpu_exact import DECODE_PATTERNS, FAMILIES, FULL, NARROW, SMALL, _skewed_experts
+from test_gpu_exact import (DECODE_PATTERNS, FAMILIES, FULL, NARROW, ODD_KB, SMALL, _skewed_experts,
+                            odd_kb_positions)
 
 
 @pytest.mark.parametrize("qt", FAMILIES)
@@ -54,3 +55,13 @@ def test_premise_odd_scales(odd):
     experts = _skewed_experts(full.E, full.T, seed=10)
     keep = np.arange(0, full.T, 16)
     check_premise(full, mats, x[keep], experts[keep])
+
+
+@pytest.mark.parametrize("cfg0", ODD_KB, ids=lambda c: c.name)
+@pytest.mark.parametrize("qt", [(2, 2, 2), (3, 3, 2), (1, 1, 1)])
+def test_premise_single_token_odd_kblocks(cfg0, qt):
+    cfg = synth.small_config(cfg0, q_gate=qt[0], q_up=qt[1], q_down=qt[2])
+    mats = exact_mats(cfg)
+    for i, pos in enumerate(odd_kb_positions(cfg.d)):
+        x, _ = basis_tokens(cfg.d, 1, seed=3000 + i, positions=[pos])
+        check_premise(cfg, mats, x, np.array([(3 * i + 1) % cfg.E]))

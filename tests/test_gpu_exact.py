@@ -38,6 +38,22 @@ FULL = synth.small_config(synth.CONFIGS["c3"], name="exact_full", T=256, E=16, k
 NARROW = synth.small_config(synth.CONFIGS["c3"], name="exact_narrow", T=400, d=768, E=12, k=1,
                             inter=384, n_shared=1, router=False, zipf_s=0.0)
 
+# single-token decode at hidden sizes of 17 and 31 k-blocks of 128: the gate/up launch
+# splits them over two waves of up to 16 k-blocks, the second wave's range ragged (the
+# clamped k-block path); decode only (prefill needs d % 256 == 0)
+ODD_KB = [synth.small_config(synth.CONFIGS["c3"], name=f"exact_kb{d // 128}", T=8, d=d, E=16,
+                             k=1, inter=256, n_shared=1, router=False, zipf_s=0.0)
+          for d in (2176, 3968)]
+
+
+def odd_kb_positions(d):
+    """Basis positions in the first and last k-block of each wave's range and in the
+    last, ragged k-block."""
+    kb = d // 128
+    half = (kb + 1) // 2
+    return [0, half * 128 - 1, half * 128, half * 128 + 77, d - 128, d - 1]
+
+
 # decode routing patterns (token -> expert): slot heights 1..8 and a 9-slot list
 DECODE_PATTERNS = [[3], [5, 5], [1, 2, 1], [7, 7, 7, 7], [0, 0, 0, 0, 0], [2, 9, 9, 9, 9, 9],
                    [4] * 7, [6] * 8, [1, 2, 3, 4, 5, 6, 7, 8], [11, 11, 11, 12, 12, 13, 13, 13]]
@@ -89,6 +105,19 @@ def test_exact_decode_full_shapes(qt):
         out, _ = _run(dl, x, lg, "decode")
         ref = oracle_outputs(cfg, 0, x, lg, np.arange(len(pat)), False, mats=mats)
         _assert_identical(out, ref, f"decode {qt} T={len(pat)}")
+
+
+@pytest.mark.parametrize("cfg0", ODD_KB, ids=lambda c: c.name)
+@pytest.mark.parametrize("qt", [(2, 2, 2), (3, 3, 2), (1, 1, 1)])
+def test_exact_single_token_decode_odd_kblocks(cfg0, qt):
+    cfg, mats, dl = _layer(cfg0, qt)
+    for i, pos in enumerate(odd_kb_positions(cfg.d)):
+        x, _ = basis_tokens(cfg.d, 1, seed=3000 + i, positions=[pos])
+        lg = top1_logits(np.array([(3 * i + 1) % cfg.E]), cfg.E)
+        print(f"[exact decode {qt} d={cfg.d}] position {pos}", flush=True)
+        out, _ = _run(dl, x, lg, "decode")
+        ref = oracle_outputs(cfg, 0, x, lg, np.arange(1), False, mats=mats)
+        _assert_identical(out, ref, f"decode {qt} d={cfg.d} position {pos}")
 
 
 @pytest.mark.parametrize("qt", FAMILIES)
