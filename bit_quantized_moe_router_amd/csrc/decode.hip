@@ -1034,6 +1034,8 @@ static int launch_proj(DecShape sh, int n_blocks, int Mmax, hipStream_t s, const
   } else {
     if (sh.ksplit == 8 && sh.kbw == 4)
       BQ_L(8, 4);
+    else if (sh.ksplit == 4 && sh.kbw == 8)
+      BQ_L(4, 8);
     else if (sh.ksplit == 16 && sh.kbw == 4)
       BQ_L(16, 4);
     else if (sh.ksplit == 8 && sh.kbw == 8)
@@ -1089,6 +1091,8 @@ static int launch_proj_mixed(DecShape sh, int n_blocks, int Mmax, hipStream_t s,
   } else {
     if (sh.ksplit == 8 && sh.kbw == 4)
       BQ_M(8, 4);
+    else if (sh.ksplit == 4 && sh.kbw == 8)
+      BQ_M(4, 8);
     else if (sh.ksplit == 16 && sh.kbw == 4)
       BQ_M(16, 4);
     else if (sh.ksplit == 8 && sh.kbw == 8)

@@ -10,8 +10,8 @@ import pytest
 import synth
 from exact_inputs import PROJ, basis_tokens, check_premise, exact_mats
 
-from test_gpu_exact import (DECODE_PATTERNS, FAMILIES, FULL, NARROW, ODD_KB, SMALL, _skewed_experts,
-                            odd_kb_positions)
+from test_gpu_exact import (DECODE_PATTERNS, FAMILIES, FULL, NARROW, ODD_KB, SMALL, WIDE_I,
+                            _skewed_experts, odd_kb_positions)
 
 
 @pytest.mark.parametrize("qt", FAMILIES)
@@ -65,3 +65,12 @@ def test_premise_single_token_odd_kblocks(cfg0, qt):
     for i, pos in enumerate(odd_kb_positions(cfg.d)):
         x, _ = basis_tokens(cfg.d, 1, seed=3000 + i, positions=[pos])
         check_premise(cfg, mats, x, np.array([(3 * i + 1) % cfg.E]))
+
+
+@pytest.mark.parametrize("qt", [(2, 2, 2), (3, 3, 2), (1, 1, 1)])
+def test_premise_separate_down(qt):
+    cfg = synth.small_config(WIDE_I, q_gate=qt[0], q_up=qt[1], q_down=qt[2])
+    mats = exact_mats(cfg)
+    for i in (0, 1, 3, 8, 9):
+        x, _ = basis_tokens(cfg.d, len(DECODE_PATTERNS[i]), seed=4000 + i)
+        check_premise(cfg, mats, x, np.array(DECODE_PATTERNS[i]))

@@ -46,6 +46,12 @@ ODD_KB = [synth.small_config(synth.CONFIGS["c3"], name=f"exact_kb{d // 128}", T=
           for d in (2176, 3968)]
 
 
+# inter above 2048: decode takes the separate down launch and the few-token combine at
+# every token count (the fused down + combine covers I <= 2048)
+WIDE_I = synth.small_config(synth.CONFIGS["c3"], name="exact_widei", T=8, d=512, E=16, k=1,
+                            inter=2560, n_shared=1, router=False, zipf_s=0.0)
+
+
 def odd_kb_positions(d):
     """Basis positions in the first and last k-block of each wave's range and in the
     last, ragged k-block."""
@@ -118,6 +124,20 @@ def test_exact_single_token_decode_odd_kblocks(cfg0, qt):
         out, _ = _run(dl, x, lg, "decode")
         ref = oracle_outputs(cfg, 0, x, lg, np.arange(1), False, mats=mats)
         _assert_identical(out, ref, f"decode {qt} d={cfg.d} position {pos}")
+
+
+@pytest.mark.parametrize("qt", [(2, 2, 2), (3, 3, 2), (1, 1, 1)])
+def test_exact_decode_separate_down_and_combine(qt):
+    cfg, mats, dl = _layer(WIDE_I, qt)
+    for i in (0, 1, 3, 8, 9):
+        pat = DECODE_PATTERNS[i]
+        experts = np.array(pat)
+        x, _ = basis_tokens(cfg.d, len(pat), seed=4000 + i)
+        lg = top1_logits(experts, cfg.E)
+        print(f"[exact decode {qt} inter={cfg.inter}] T={len(pat)} experts={pat}", flush=True)
+        out, _ = _run(dl, x, lg, "decode")
+        ref = oracle_outputs(cfg, 0, x, lg, np.arange(len(pat)), False, mats=mats)
+        _assert_identical(out, ref, f"decode {qt} inter={cfg.inter} T={len(pat)}")
 
 
 @pytest.mark.parametrize("qt", FAMILIES)
