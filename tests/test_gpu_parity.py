@@ -468,6 +468,24 @@ def test_small_decode_router_every_T(layers):
         assert_parity(outs[bq.MOE_ADD_RESIDUAL], ref1, f"small router T={T} residual")
 
 
+WIDE_E = [synth.small_config(synth.CONFIGS["c0"], name="wide_e1000", E=1000, k=6, n_shared=1,
+                             T=8),
+          synth.small_config(synth.CONFIGS["c0"], name="wide_e1024", E=1024, k=32, n_shared=1,
+                             T=2)]
+
+
+@pytest.mark.parametrize("cfg", WIDE_E, ids=lambda c: c.name)
+def test_many_experts_router(layers, cfg):
+    """More than 256 experts (E = 1000, not a multiple of the wave; E = 1024 with the
+    largest top-k, 32) through the router: the top-k with 16 entries per lane, the
+    single-token decode with its selection in the select kernel, several tokens up to
+    T*k = 64, and prefill."""
+    dl = layers(cfg.name, cfg)
+    for T in sorted({1, cfg.T}):
+        _full_check(dl, synth.gen_x(cfg, seed=300 + T, T=T), "decode", label=f"{cfg.name} T={T}")
+    _full_check(dl, synth.gen_x(cfg, seed=399, T=100), "prefill", label=f"{cfg.name} prefill")
+
+
 @pytest.mark.parametrize("q", [synth.QT_INT2, synth.QT_TERNARY])
 @pytest.mark.parametrize("T", [37, 300])
 def test_prefill_router_ragged(layers, q, T):
