@@ -486,6 +486,23 @@ def test_many_experts_router(layers, cfg):
     _full_check(dl, synth.gen_x(cfg, seed=399, T=100), "prefill", label=f"{cfg.name} prefill")
 
 
+MAX_DIMS = synth.small_config(synth.CONFIGS["c0"], name="max_dims", d=8192, inter=8192, E=4,
+                              k=2, n_shared=1, T=3)
+
+
+@pytest.mark.timeout(600)
+def test_largest_decode_dims(layers):
+    """d = I = 8192, the largest the decode path takes: single-token gate/up on eight
+    waves of 8 k-blocks, the down projection on sixteen waves of 4 (I > 2048: separate
+    down launch and the few-token combine), several rows on eight waves of 8; and
+    prefill at the same dimensions."""
+    dl = layers("max_dims", MAX_DIMS)
+    for T in (1, 3):
+        _full_check(dl, synth.gen_x(MAX_DIMS, seed=500 + T, T=T), "decode",
+                    flags=bq.MOE_ADD_RESIDUAL, label=f"max dims T={T}")
+    _full_check(dl, synth.gen_x(MAX_DIMS, seed=510, T=40), "prefill", label="max dims prefill")
+
+
 @pytest.mark.parametrize("q", [synth.QT_INT2, synth.QT_TERNARY])
 @pytest.mark.parametrize("T", [37, 300])
 def test_prefill_router_ragged(layers, q, T):
