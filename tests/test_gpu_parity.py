@@ -234,6 +234,37 @@ def test_per_expert_mixed_precision_decode(layers, alt_q):
     assert ei.value.status == bq.MOE_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("alt_q", [(2, 2, 2), (2, 1, 1)])
+def test_mixed_precision_decode_wide(layers, alt_q):
+    """The per-expert second copy at d = 4096: the single-token gate/up launch over both
+    copies (or one per copy) on two waves of 16 k-blocks, and T = 3."""
+    src = synth.small_config(MULTI, name="mixwide_src", d=4096, inter=256, q_gate=synth.QT_INT3,
+                             q_up=synth.QT_INT3, q_down=synth.QT_INT2, T=3)
+    main = layers("mixwide_main", src)
+    alt = layers(f"mixwide_alt{alt_q}",
+                 workloads.DeviceLayer(src, 0, DEV, shadow_qtypes=alt_q))
+    ids1 = oracle.topk_softmax(synth.gen_logits(src, T=1), src.k)[0][0]
+    sel_np = np.zeros(src.E, np.uint8)
+    sel_np[ids1[0]] = sel_np[ids1[2]] = 1  # the single token reads both copies
+    h = bq.make_layer(src.d, src.inter, src.E, src.k, src.n_shared, src.qtypes, main.experts,
+                      main.stride, main.shared, main.router_w, main.router_bias,
+                      alt=(alt.experts, alt.stride, alt_q, torch.from_numpy(sel_np).to(DEV)))
+    dl = types.SimpleNamespace(cfg=src, layer=0, handle=h)
+    shadow = shadow_mats(src, alt_q, 0)
+
+    def mats(e):
+        if e < src.E and sel_np[e]:
+            return shadow(e)
+        return [synth.gen_matrix(src, 0, e, m) for m in range(3)]
+
+    def qtypes_of(e):
+        return alt_q if e < src.E and sel_np[e] else src.qtypes
+
+    for T in (1, 3):
+        _full_check(dl, synth.gen_x(src, T=T), "decode", logits=synth.gen_logits(src, T=T),
+                    label=f"mixed wide {alt_q}", mats=mats, qtypes_of=qtypes_of)
+
+
 def test_prefill_int3_mixed(layers):
     cfg = synth.small_config(MULTI, name="int3mix", q_gate=synth.QT_INT3, q_up=synth.QT_INT2,
                              q_down=synth.QT_INT3, T=300)
