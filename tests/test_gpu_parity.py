@@ -499,6 +499,20 @@ def test_small_decode_router_every_T(layers):
         assert_parity(outs[bq.MOE_ADD_RESIDUAL], ref1, f"small router T={T} residual")
 
 
+@pytest.mark.parametrize("q", [synth.QT_INT2, synth.QT_TERNARY, synth.QT_INT3])
+def test_prefill_few_tokens(layers, q):
+    """Prefill at T = 1, 2 and 5 (a partial 32-row sub-tile per expert, the few-token
+    combine) through the router, with and without the residual, for each code family:
+    the 8-wave 2-bit and ternary GEMMs (d = 512, inter = 256) and the bf16-operand one."""
+    cfg = synth.small_config(SMALL_ROUTER, name=f"few_{q}", d=512, inter=256, E=16, k=4,
+                             q_gate=q, q_up=q, q_down=q)
+    dl = layers(cfg.name, cfg)
+    for T in (1, 2, 5):
+        x = synth.gen_x(cfg, seed=600 + T, T=T)
+        for flags in (0, bq.MOE_ADD_RESIDUAL):
+            _full_check(dl, x, "prefill", flags=flags, label=f"few tokens q={q} T={T}")
+
+
 WIDE_E = [synth.small_config(synth.CONFIGS["c0"], name="wide_e1000", E=1000, k=6, n_shared=1,
                              T=8),
           synth.small_config(synth.CONFIGS["c0"], name="wide_e1024", E=1024, k=32, n_shared=1,
