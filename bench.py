@@ -152,7 +152,8 @@ def decode_leg(args, dev):
         return ((int(act.sum()) - n_alt_act + cfg.n_shared) * per(fam[False]) +
                 n_alt_act * (per(fam[True]) if n_alt_act else 0))
     n = W + K
-    X = synth.gen_x(cfg, T=T * n).reshape(n, T, cfg.d)
+    n_tok = max(n, C)  # the per-copy kernel timings below take token j for copy j
+    X = synth.gen_x(cfg, T=T * n_tok).reshape(n_tok, T, cfg.d)
     xd = torch.from_numpy(X.view(np.int16)).to(dev)
     R = bq.alloc_routing(T, cfg.E, cfg.k, dev)
     ws = bq.alloc_workspace(handles[0], T, dev)
