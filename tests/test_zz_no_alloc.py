@@ -1,9 +1,10 @@
 """moe_forward_decode_noalloc (workspace in the library's static device array)
 against moe_forward_decode (caller's workspace): the same kernels, so every
 output -- the layer's and the routing's -- must be identical bit for bit.
-Two calls in a row on the array, the second with fewer tokens (the array keeps
-the first call's contents), then a call at other shapes; one call is also
-checked against the oracle."""
+Calls in a row on the array with fewer tokens after the first (the array keeps
+the previous call's contents; the single-token call takes its selection inside
+gate/up), then a call at other shapes; one call is also checked against the
+oracle."""
 import numpy as np
 import pytest
 import torch
@@ -47,7 +48,7 @@ def _both(dl, x_np, flags):
 
 def test_noalloc_decode_matches_decode():
     dl = workloads.DeviceLayer(CFG, 0, DEV)
-    for T, flags in ((8, 0), (3, bq.MOE_ADD_RESIDUAL)):
+    for T, flags in ((8, 0), (1, 0), (3, bq.MOE_ADD_RESIDUAL)):
         print(f"[noalloc] c2 shapes E=32 T={T} flags={flags}", flush=True)
         x = synth.gen_x(CFG, seed=500 + T, T=T)
         out, r = _both(dl, x, flags)
